@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the Periodic Row-wise Muon optimizer step on one MI355X.
+
+One step is a full optimizer step of the whole parameter set (momentum, the
+branch direction - NS5 on refresh steps, gamma * RowNorm otherwise - and the
+weight update; plus AdamW on the per-block bias vectors).  Throughput is
+optimizer steps/s averaged over whole K-cycles (the cycle average of paper
+Eq. (9) in the PaperDaily post on "Scaling Muon for Diffusion Transformers").
+
+Inputs are seeded synthetic DiT-shaped weights and bf16 gradients, resident
+in HBM before the timed region.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import workloads  # noqa: E402
+
+METRIC = "optimizer steps/s (K=3 cycle avg); NS5 MFMA %peak; RowNorm HBM GB/s"
+PEAK_BF16 = 2.5e15        # dense bf16 MFMA, FLOP/s
+PEAK_F32 = 157.3e12       # dense fp32 MFMA, FLOP/s
+PEAK_HBM = 8.0e12         # bytes/s
+ROWNORM_BYTES = 18        # per element: read G bf16 2 + M 4 + W 4, write M 4 + W 4
+
+
+def ns5_class_flops(shapes, iters=5):
+    """Algorithmic flops per refresh step, per kernel class.
+
+    Per matrix and iteration (r short side, c long side): symmetric Gram
+    r^2 c, symmetric A^2 r^3, product 2 r^2 c.
+    """
+    g = p = x = 0.0
+    for m, n in shapes:
+        r, c = min(m, n), max(m, n)
+        g += r * r * c
+        p += float(r) ** 3
+        x += 2.0 * r * r * c
+    return {"ns_gram": iters * g, "ns_poly": iters * p, "ns_product": iters * x}
+
+
+def rownorm_class_bytes(shapes, gbytes):
+    """Algorithmic bytes per RowNorm step per kernel class (long-axis mode)."""
+    rows = cols1 = cols2 = 0
+    for m, n in shapes:
+        e = m * n
+        if m > n:
+            cols1 += (gbytes + 8) * e      # read G, M; write M
+            cols2 += 12 * e                # read M, W; write W
+        else:
+            rows += (gbytes + 16) * e
+    return {"rownorm_rows": rows, "rownorm_cols1": cols1, "rownorm_cols2": cols2}
+
+
+def cpu_baseline(wl, cfg_over, sample_blocks=1):
+    """The fp64 oracle as it stands, one K-cycle on a sample of blocks."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    ocfg = oracle.OracleConfig(**cfg_over)
+    per_block = len(workloads.dit_block_shapes(wl.d)) if wl.d else len(wl.shapes)
+    shapes = [(m, n) for _, m, n in wl.shapes[:per_block * sample_blocks]]
+    W = [workloads.host_weight0(0, i, s).astype(np.float64) for i, s in enumerate(shapes)]
+    M = [np.zeros(s) for s in shapes]
+    G = [workloads.host_grad(0, 0, i, s, wl.grad_std, wl.grad_dtype) for i, s in enumerate(shapes)]
+    K = ocfg.K if ocfg.bp_blocks == 0 else ocfg.bp_period
+    t0 = time.perf_counter()
+    for t in range(K):
+        for i in range(len(shapes)):
+            W[i], M[i], _ = oracle.muon_matrix_step(W[i], M[i], G[i], t, ocfg)
+    dt = time.perf_counter() - t0
+    scale = (wl.blocks / sample_blocks) if wl.blocks else 1.0
+    steps_per_s = K / (dt * scale)
+    return {"value": steps_per_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(shapes)} matrices ({sample_blocks} of {wl.blocks or 1} blocks), one "
+                      f"{K}-step cycle, {dt:.1f} s, scaled x{scale:g} to the whole set",
+            "sample_seconds": dt}
+
+
+def copy_calibration(nbytes: int, reps: int) -> None:
+    """A plain device copy of known size, for scaling HBM counters."""
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dit-1.3b", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--ns-precision", choices=["bf16", "f32"], default="bf16")
+    ap.add_argument("--K", type=int, default=None, help="refresh period (default 3)")
+    ap.add_argument("--no-adamw", action="store_true", help="leave out the bias vectors")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=1)
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--ws-gib", type=float, default=None, help="NS5 workspace cap (GiB)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES bytes (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the optimizer step is measured on one "
+              "MI355X at the full per-GPU matrix shapes; --gpus must be 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import matrix_aware_optimizer_periodic_amd as mm
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return 0
+
+    wl = workloads.WORKLOADS[args.workload]
+    over = dict(wl.overrides)
+    if args.K is not None:
+        over["K"] = args.K
+    over["ns_precision"] = mm.MUON_NS_BF16 if args.ns_precision == "bf16" else mm.MUON_NS_F32
+    if args.ws_gib is not None:
+        over["ns_workspace_max"] = int(args.ws_gib * 2 ** 30)
+    cfg = mm.muon_config_default(**over)
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    shapes = [(m, n) for _, m, n in wl.shapes]
+    gdt = torch.bfloat16 if wl.grad_dtype == "bf16" else torch.float32
+    params, grads = [], []
+    for i, s in enumerate(shapes):
+        params.append(workloads.device_normal_(torch.empty(s, device=dev), 0.02,
+                                               workloads.seed_for(0, 0, i, 2)))
+        grads.append(workloads.device_normal_(torch.empty(s, dtype=gdt, device=dev),
+                                              wl.grad_std, workloads.seed_for(0, 0, i, 1)))
+    kinds = [mm.MUON_KIND_MATRIX] * len(shapes)
+    n_bias = 0
+    bias_elems = 0
+    if not args.no_adamw and wl.d:
+        for b in range(wl.blocks):
+            for j, L in enumerate(workloads.dit_bias_sizes(wl.d)):
+                params.append(workloads.device_normal_(torch.empty(L, device=dev), 0.02,
+                                                       workloads.seed_for(0, b, j, 3)))
+                grads.append(workloads.device_normal_(torch.empty(L, dtype=gdt, device=dev),
+                                                      wl.grad_std, workloads.seed_for(0, b, j, 4)))
+                kinds.append(mm.MUON_KIND_ADAMW)
+                n_bias += 1
+                bias_elems += L
+    stream = torch.cuda.current_stream(dev)
+    sess = mm.MuonSession(params, grads, kinds=kinds, cfg=cfg, stream=stream)
+    torch.cuda.synchronize()
+
+    K = cfg.K if cfg.bp_blocks == 0 else cfg.bp_period
+    for t in range(args.warmup):
+        sess.step(t)
+    torch.cuda.synchronize()
+    if not args.no_kernel_timing:
+        mm.muon_timing_read(sess.ctx)          # discard warm-up records
+        mm.muon_timing_enable(sess.ctx, True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        sess.step(args.warmup + k)
+    starts[args.steps].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_ms = [starts[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
+    total_ms = sum(step_ms)
+    kt = mm.muon_timing_read(sess.ctx) if not args.no_kernel_timing else {}
+    mm.muon_timing_enable(sess.ctx, False)
+
+    branches = [sess.branch(args.warmup + k) for k in range(args.steps)]
+    by_branch = {}
+    for b, ms in zip(branches, step_ms):
+        by_branch.setdefault(b, []).append(ms)
+    names = {0: "rownorm", 1: "ns5", 2: "block_ns5"}
+    branch_ms = {names[b]: float(np.mean(v)) for b, v in by_branch.items()}
+    n_refresh = branches.count(mm.MUON_BRANCH_NS5)
+
+    # ---- NS5 and RowNorm figures -------------------------------------------
+    peak_mm = PEAK_BF16 if args.ns_precision == "bf16" else PEAK_F32
+    fl = ns5_class_flops(shapes, cfg.ns_iters)
+    f_refresh = sum(fl.values())
+    ns5 = None
+    if "ns5" in branch_ms:
+        tf = f_refresh / (branch_ms["ns5"] * 1e-3)
+        ns5 = {"step_ms": branch_ms["ns5"], "tflops": tf / 1e12, "frac": tf / peak_mm,
+               "flops_alg": f_refresh}
+    elems = sum(m * n for m, n in shapes)
+    gbytes = 2 if gdt == torch.bfloat16 else 4
+    rown = None
+    if "rownorm" in branch_ms:
+        bps = (gbytes + 16) * elems / (branch_ms["rownorm"] * 1e-3)
+        rown = {"step_ms": branch_ms["rownorm"], "gbps": bps / 1e9, "frac": bps / PEAK_HBM,
+                "bytes_alg": (gbytes + 16) * elems}
+
+    roofline = None
+    kernels = {}
+    if kt:
+        nb = rownorm_class_bytes(shapes, gbytes)
+        n_rn = branches.count(mm.MUON_BRANCH_ROWNORM)
+        for name, (ms, cnt) in kt.items():
+            if cnt == 0:
+                continue
+            rec = {"total_ms": ms, "launches": cnt, "avg_ms": ms / cnt}
+            if name in fl and n_refresh:
+                per = fl[name] * n_refresh / cnt
+                rec.update(bound="mfma", work_per_launch=per, achieved=per / (ms / cnt * 1e-3) / 1e12,
+                           unit="TFLOP/s", peak=peak_mm / 1e12)
+            elif name in nb and n_rn:
+                per = nb[name] * n_rn / cnt
+                rec.update(bound="hbm", work_per_launch=per, achieved=per / (ms / cnt * 1e-3) / 1e9,
+                           unit="GB/s", peak=PEAK_HBM / 1e9)
+            if "achieved" in rec:
+                rec["frac"] = rec["achieved"] / rec["peak"]
+            kernels[name] = rec
+        dom = max((k for k in kernels if "achieved" in kernels[k]),
+                  key=lambda k: kernels[k]["total_ms"], default=None)
+        if dom:
+            r = kernels[dom]
+            roofline = {"kernel": dom, "bound": r["bound"], "achieved": r["achieved"],
+                        "peak": r["peak"], "unit": r["unit"], "frac": r["frac"],
+                        "traffic": None, "avg_launch_ms": r["avg_ms"],
+                        "work_per_launch": r["work_per_launch"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        ocfg = {k: v for k, v in over.items() if k in ("K", "bp_blocks", "bp_period", "bp_lr_ratio")}
+        cpu = cpu_baseline(wl, ocfg, args.cpu_sample_blocks)
+
+    value = args.steps / (total_ms * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.ns_precision,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "d": wl.d, "blocks": wl.blocks, "matrices": len(shapes),
+            "matrix_elements": elems, "grad_dtype": wl.grad_dtype, "state_dtype": "f32",
+            "K": cfg.K, "gamma": round(cfg.gamma, 6), "lr": round(cfg.lr, 6),
+            "beta": round(cfg.beta, 6), "eps_row": cfg.eps_row,
+            "ns_iters": cfg.ns_iters, "ns_coeffs": [round(cfg.ns_a, 6), round(cfg.ns_b, 6),
+                                                    round(cfg.ns_c, 6)],
+            "ns_eps": cfg.ns_eps, "ns_prenorm": "X / (||X||_F + ns_eps)",
+            "ns_precision": args.ns_precision, "rownorm_axis": "long" if cfg.rownorm_axis == 0 else "rows",
+            "bp_blocks": cfg.bp_blocks, "adamw_tensors": n_bias, "adamw_elements": bias_elems,
+            "ns_workspace_max": int(cfg.ns_workspace_max), "state_bytes": sess.state_bytes,
+        },
+        "branch_ms": branch_ms,
+        "ns5": ns5,
+        "rownorm": rown,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "wall_s": wall,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out))
+    sess.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

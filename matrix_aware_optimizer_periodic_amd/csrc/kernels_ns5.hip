@@ -1,0 +1,520 @@
+// Refresh step: momentum, Frobenius pre-normalisation and the Newton-Schulz
+// iteration as batched MFMA GEMMs.
+//
+// "Scaling Muon for Diffusion Transformers" (abstract) and the PaperDaily
+// post's section "Periodic Row-wise Muon" (text under blog fig. 3): on steps
+// with t mod K == 0 the direction is NS5(M), five rounds of matrix products
+// that push M towards its polar factor without an SVD.  Per round, on the
+// wide orientation X (r x c, r <= c):
+//
+//     A = X X^T          (r x r x c, symmetric: upper tiles only, mirrored)
+//     B = b A + c A A    (r x r x r, symmetric)
+//     X = a X + B X      (r x c x r)
+//
+// and the last round writes W -= lr * X straight into the stored layout.
+//
+// Layout.  X lives in the workspace twice: Xr (r x c, row-major) and Xc
+// (c x r, row-major, i.e. X^T).  Every product is then of the form
+// C[i][j] = sum_k P[i][k] Q[j][k] with both operands contiguous along k:
+// Gram P = Q = Xr; poly P = Q = A (symmetric); product P = B, Q = Xc.  The
+// product epilogue writes the new X into both layouts (Xr in place, Xc
+// ping-pong).  A tall stored matrix (m > n) is X^T, so it is read and
+// written through the same two layouts: no separate transpose pass.
+// All workspace dims are padded to the tile size with zeros; zero padding is
+// preserved exactly by the three products, so the GEMMs need no bounds
+// checks and ragged shapes cost only the padded tiles.
+#include <hip/hip_runtime.h>
+
+#include "muon_internal.h"
+
+namespace muon {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__device__ __forceinline__ float load_g(const void* g, int gdt, int64_t idx) {
+  if (gdt == 1) return bf16_to_f32(static_cast<const uint16_t*>(g)[idx]);
+  return static_cast<const float*>(g)[idx];
+}
+
+// ---------------------------------------------------------------------------
+// Momentum over one NS problem's stored block, kMomRowsPerPart rows per
+// workgroup, plus that slab's sum of squares (one partial per workgroup).
+__global__ __launch_bounds__(kThreads) void ns_momentum_kernel(
+    const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
+    const TileItem* __restrict__ items, float beta) {
+  __shared__ float red[4];
+  const TileItem it = items[blockIdx.x];
+  const NsDev d = ns[it.id];
+  const MatDev mt = mats[d.mat];
+  const int64_t r0 = int64_t(it.ti) * d.rows_per_part;
+  const int64_t r1 = min(d.rows, r0 + d.rows_per_part);
+  float ss = 0.f;
+  const bool vec = ((d.ld | d.col0 | d.cols) & 3) == 0;
+  if (vec) {
+    const int64_t n4 = d.cols >> 2;
+    for (int64_t r = r0; r < r1; ++r) {
+      const int64_t base = r * d.ld + d.col0;
+      for (int64_t q = threadIdx.x; q < n4; q += kThreads) {
+        const int64_t e = base + 4 * q;
+        float4 g;
+        if (mt.gdt == 1) {
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(mt.g) + e);
+          g = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
+                          bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
+        } else {
+          g = *reinterpret_cast<const float4*>(static_cast<const float*>(mt.g) + e);
+        }
+        float4 m = *reinterpret_cast<const float4*>(mt.mom + e);
+        m = make_float4(fmaf(beta, m.x, g.x), fmaf(beta, m.y, g.y), fmaf(beta, m.z, g.z),
+                        fmaf(beta, m.w, g.w));
+        *reinterpret_cast<float4*>(mt.mom + e) = m;
+        ss += m.x * m.x + m.y * m.y + m.z * m.z + m.w * m.w;
+      }
+    }
+  } else {
+    for (int64_t r = r0; r < r1; ++r) {
+      const int64_t base = r * d.ld + d.col0;
+      for (int64_t q = threadIdx.x; q < d.cols; q += kThreads) {
+        const int64_t e = base + q;
+        const float m = fmaf(beta, mt.mom[e], load_g(mt.g, mt.gdt, e));
+        mt.mom[e] = m;
+        ss += m * m;
+      }
+    }
+  }
+  const float tot = block_sum(ss, red);
+  if (threadIdx.x == 0) d.part[it.ti] = tot;
+}
+
+// 1 / (||M||_F + eps) per NS problem, partials added in a fixed order.
+__global__ __launch_bounds__(kThreads) void ns_scale_kernel(NsDev* __restrict__ ns, float eps) {
+  __shared__ float red[4];
+  const NsDev d = ns[blockIdx.x];
+  float s = 0.f;
+  for (int k = threadIdx.x; k < d.nparts; k += kThreads) s += d.part[k];
+  const float tot = block_sum(s, red);
+  if (threadIdx.x == 0) d.scale[0] = 1.0f / (sqrtf(tot) + eps);
+}
+
+// X0 = M * scale, cast to the workspace type and written in both layouts.
+// One 64 x 64 tile of the padded stored block per workgroup; elements
+// outside the logical block are written as zeros.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void ns_cast_kernel(
+    const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
+    const TileItem* __restrict__ items) {
+  __shared__ float tile[kPrepTile][kPrepTile + 1];
+  const TileItem it = items[blockIdx.x];
+  const NsDev d = ns[it.id];
+  const float* __restrict__ mom = mats[d.mat].mom;
+  const float sc = d.scale[0];
+  const int64_t p0 = int64_t(it.ti) * kPrepTile, q0 = int64_t(it.tj) * kPrepTile;
+  // direct copy (stored orientation) and transposed copy
+  T* dst = static_cast<T*>(d.tall ? d.xc[0] : d.xr);
+  const int64_t ldd = d.tall ? d.rp : d.cp;
+  T* dstt = static_cast<T*>(d.tall ? d.xr : d.xc[0]);
+  const int64_t ldt = d.tall ? d.cp : d.rp;
+  const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int lr = tr + 16 * pass;
+    const int64_t p = p0 + lr;
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t q = q0 + tc + u;
+      v[u] = (p < d.rows && q < d.cols) ? mom[p * d.ld + d.col0 + q] * sc : 0.f;
+      tile[lr][tc + u] = v[u];
+    }
+    T* o = dst + p * ldd + q0 + tc;
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      const uint32_t hi = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<u32x2_t*>(o) = u32x2_t{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int lq = tr + 16 * pass;
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = tile[tc + u][lq];
+    T* o = dstt + (q0 + lq) * ldt + p0 + tc;
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      const uint32_t hi = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<u32x2_t*>(o) = u32x2_t{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Eight consecutive workspace values as fp32 (16 bytes of bf16 or 32 of fp32,
+// always aligned: workspace rows are padded to the tile size).
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float v[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = bf16_to_f32(u[k] & 0xffffu);
+      v[2 * k + 1] = bf16_to_f32(u[k] >> 16);
+    }
+  } else {
+    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
+    const f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { v[k] = a[k]; v[4 + k] = b[k]; }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float v[8]) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4_t u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) u[k] = f32_to_bf16(v[2 * k]) | (f32_to_bf16(v[2 * k + 1]) << 16);
+    *reinterpret_cast<u32x4_t*>(p) = u;
+  } else {
+    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// W[e0 + u] = W[e0 + u] * keep - lr * v[u] for u < nv (the weight update of the
+// last Newton-Schulz round), vectorised when the run is whole and aligned.
+__device__ __forceinline__ void w_update8(float* w, int64_t e0, int nv, const float v[8], float lr,
+                                          float keep) {
+  if (nv == 8 && (e0 & 3) == 0) {
+    f32x4_t a = reinterpret_cast<f32x4_t*>(w + e0)[0];
+    f32x4_t b = reinterpret_cast<f32x4_t*>(w + e0)[1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k] = fmaf(-lr, v[k], a[k] * keep);
+      b[k] = fmaf(-lr, v[4 + k], b[k] * keep);
+    }
+    reinterpret_cast<f32x4_t*>(w + e0)[0] = a;
+    reinterpret_cast<f32x4_t*>(w + e0)[1] = b;
+  } else {
+    for (int u = 0; u < nv; ++u) w[e0 + u] = fmaf(-lr, v[u], w[e0 + u] * keep);
+  }
+}
+
+// GEMM tile C[i0.., j0..] = sum_k P[i][k] Q[j][k] on MFMA, BM x BM per
+// workgroup of 4 waves (2 x 2), each wave (BM/2) x (BM/2) built from 32 x 32
+// MFMA blocks.  The k loop stages 128-byte rows (64 bf16 or 32 fp32) of P and
+// Q through LDS, double-buffered, with the 16-byte chunks of each row XOR-
+// swizzled by (row & 7) so the fragment reads of 32 consecutive rows hit
+// distinct banks.
+//
+// MFMA operand layout used (both 32 x 32 variants): lane l supplies row
+// (l & 31) of P and of Q; its k values are the 16-byte chunk 2g + (l >> 5) of
+// k-group g.  bf16 32x32x16 consumes the chunk's 8 values at once; fp32
+// 32x32x2 consumes its 4 values over 4 instructions.  Any pairing of k
+// between the two operands is valid as long as it is the same for both.
+// Accumulator element v of lane l is C[8 (v/4) + 4 (l/32) + (v%4)][l & 31].
+//
+// Epilogue, per half of the tile's rows: the owning waves park their
+// accumulators in LDS, then all threads write the outputs in 16-byte chunks,
+// first along rows (C, or W of a wide matrix), then along columns (the
+// mirrored half of a symmetric A or B, X^T, or W of a tall matrix).
+//
+// Rounding.  The diagonals of A and B stay in fp32 (adiag, bdiag): B's
+// diagonal is applied as (a + B_ii) X_i in fp32 and stored as 0 in the bf16
+// operand, and the A_ii^2 term of (A A)_ii and the b A_ii term use the fp32
+// A_ii.  This is the same arithmetic, rounded later: it avoids the
+// cancellation between a and B_ii that bf16 storage of B_ii would amplify
+// when the short side r is small.
+template <typename T, int BM, int OP>
+__global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
+    const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
+    const GemmItem* __restrict__ items, int iter, int last, float ca, float cb, float cc,
+    float wd) {
+  constexpr int WM = BM / 2;
+  constexpr int FM = WM / 32;
+  constexpr int ROWS = 2 * BM;               // P rows then Q rows
+  constexpr int LOADS = ROWS * 8 / kThreads; // 16-byte loads per thread per stage
+  constexpr int KT = 128 / int(sizeof(T));   // k elements per stage
+  constexpr int SLD = BM + 4;                // epilogue stage row stride (floats)
+  constexpr int MAIN_BYTES = 2 * ROWS * 128;
+  constexpr int STAGE_BYTES = WM * SLD * 4;
+  constexpr int SMEM = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  u32x4_t* lds = reinterpret_cast<u32x4_t*>(smem);
+
+  const GemmItem it = items[blockIdx.x];
+  const NsDev d = ns[it.ns];
+  const int cur = iter & 1;
+  const T* P;
+  const T* Q;
+  int64_t ld, K;
+  if constexpr (OP == kGemmGram) {
+    P = Q = static_cast<const T*>(d.xr); ld = d.cp; K = d.cp;
+  } else if constexpr (OP == kGemmPoly) {
+    P = Q = static_cast<const T*>(d.a); ld = d.rp; K = d.rp;
+  } else {
+    P = static_cast<const T*>(d.b); Q = static_cast<const T*>(d.xc[cur]); ld = d.rp; K = d.rp;
+  }
+  const int64_t i0 = int64_t(it.ti) * BM, j0 = int64_t(it.tj) * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+
+  // Global -> LDS mapping: load L covers LDS rows 32 L .. 32 L + 31.
+  const int lrow = tid >> 3, lch = tid & 7;
+  const char* gP = reinterpret_cast<const char*>(P + (i0 + lrow) * ld) + lch * 16;
+  const char* gQ = reinterpret_cast<const char*>(Q + (j0 + lrow) * ld) + lch * 16;
+  const int64_t gstride = 32 * ld * int64_t(sizeof(T));
+  const int sofs = lrow * 8 + (lch ^ (lrow & 7));
+
+  u32x4_t stg[LOADS];
+  auto gload = [&](int kt) {
+    const int64_t kb = int64_t(kt) * 128;
+#pragma unroll
+    for (int L = 0; L < LOADS; ++L) {
+      const char* src = (L < LOADS / 2) ? gP + L * gstride : gQ + (L - LOADS / 2) * gstride;
+      stg[L] = *reinterpret_cast<const u32x4_t*>(src + kb);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int L = 0; L < LOADS; ++L) lds[buf * ROWS * 8 + L * 256 + sofs] = stg[L];
+  };
+
+  f32x16_t acc[FM][FM];
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FM; ++b) acc[a][b] = (f32x16_t)(0.0f);
+
+  const int nk = int(K / KT);
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int frow = lane & 31, fsw = lane & 7, fhalf = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const u32x4_t* sP = lds + buf * ROWS * 8;
+    const u32x4_t* sQ = sP + BM * 8;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ch = (2 * g + fhalf) ^ fsw;
+      u32x4_t af[FM], bfr[FM];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        af[f] = sP[(wm * WM + f * 32 + frow) * 8 + ch];
+        bfr[f] = sQ[(wn * WM + f * 32 + frow) * 8 + ch];
+      }
+#pragma unroll
+      for (int fa = 0; fa < FM; ++fa)
+#pragma unroll
+        for (int fb = 0; fb < FM; ++fb) {
+          if constexpr (sizeof(T) == 2) {
+            acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, af[fa]), __builtin_bit_cast(bf16x8_t, bfr[fb]),
+                acc[fa][fb], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                  __uint_as_float(af[fa][s]), __uint_as_float(bfr[fb][s]), acc[fa][fb], 0, 0, 0);
+          }
+        }
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue -----------------------------------------------------------
+  float* stage = reinterpret_cast<float*>(smem);
+  const bool diag_tile = it.ti == it.tj;
+  T* xr = static_cast<T*>(d.xr);
+  T* xcn = static_cast<T*>(d.xc[cur ^ 1]);
+  float* w = mats[d.mat].w;
+  const float wkeep = 1.0f - d.lr * wd;
+  bool mirror;
+  if constexpr (OP == kGemmProduct) mirror = !last || d.tall;
+  else mirror = !diag_tile;
+
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int fa = 0; fa < FM; ++fa)
+#pragma unroll
+        for (int fb = 0; fb < FM; ++fb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            stage[(fa * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3)) * SLD + wn * WM + fb * 32 + frow] =
+                acc[fa][fb][v];
+    }
+    __syncthreads();
+    const int64_t ib0 = i0 + int64_t(half) * WM;
+    // rows of the tile: C[i][j .. j+7]
+    constexpr int CPR = BM / 8;
+    for (int idx = tid; idx < WM * CPR; idx += kThreads) {
+      const int r = idx / CPR, ch = idx % CPR;
+      const int64_t i = ib0 + r, j = j0 + ch * 8;
+      float* sv = stage + r * SLD + ch * 8;
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = sv[u];
+      const bool has_diag = diag_tile && i >= j && i < j + 8;
+      if constexpr (OP == kGemmGram) {
+        if (has_diag) d.adiag[i] = v[i - j];
+        store8(static_cast<T*>(d.a) + i * d.rp + j, v);
+      } else if constexpr (OP == kGemmPoly) {
+        float av[8];
+        load8(static_cast<const T*>(d.a) + i * d.rp + j, av);
+        float dval = 0.f;
+        if (has_diag) {
+          const int u = int(i - j);
+          const float ad = d.adiag[i];
+          const float aa = v[u] + ad * ad - av[u] * av[u];
+          dval = fmaf(cb, ad, cc * aa);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = fmaf(cc, v[u], cb * av[u]);
+        if (has_diag) {
+          v[i - j] = 0.f;
+          d.bdiag[i] = dval;
+        }
+        store8(static_cast<T*>(d.b) + i * d.rp + j, v);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sv[u] = v[u];
+      } else {
+        float xv[8];
+        load8(xr + i * d.cp + j, xv);
+        const float mlt = ca + d.bdiag[i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = fmaf(mlt, xv[u], v[u]);
+        if (!last) {
+          store8(xr + i * d.cp + j, v);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sv[u] = v[u];
+        } else if (!d.tall) {
+          if (i < d.r) {
+            const int nv = int(max<int64_t>(0, min<int64_t>(8, d.c - j)));
+            if (nv > 0) w_update8(w, i * d.ld + d.col0 + j, nv, v, d.lr, wkeep);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sv[u] = v[u];
+        }
+      }
+    }
+    __syncthreads();
+    // columns of the tile: C[i .. i+7][j] written as row j of the transpose
+    if (mirror) {
+      constexpr int CPC = WM / 8;
+      for (int idx = tid; idx < BM * CPC; idx += kThreads) {
+        const int jj = idx / CPC, ch = idx % CPC;
+        const int64_t j = j0 + jj, i = ib0 + ch * 8;
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = stage[(ch * 8 + u) * SLD + jj];
+        if constexpr (OP == kGemmGram) {
+          store8(static_cast<T*>(d.a) + j * d.rp + i, v);
+        } else if constexpr (OP == kGemmPoly) {
+          store8(static_cast<T*>(d.b) + j * d.rp + i, v);
+        } else {
+          if (!last) {
+            store8(xcn + j * d.rp + i, v);
+          } else if (j < d.c) {
+            const int nv = int(max<int64_t>(0, min<int64_t>(8, d.r - i)));
+            if (nv > 0) w_update8(w, j * d.ld + d.col0 + i, nv, v, d.lr, wkeep);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, int BM>
+hipError_t launch_gemm_t(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                         const GemmItem* items, int64_t nitems, int op, int iter, int last,
+                         float a, float b, float c, float wd) {
+  const dim3 grid(static_cast<unsigned>(nitems)), block(kThreads);
+  switch (op) {
+    case kGemmGram:
+      ns_gemm_kernel<T, BM, kGemmGram><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      break;
+    case kGemmPoly:
+      ns_gemm_kernel<T, BM, kGemmPoly><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      break;
+    default:
+      ns_gemm_kernel<T, BM, kGemmProduct><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ns_momentum(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                              const TileItem* items, int64_t nitems, float beta) {
+  if (nitems <= 0) return hipSuccess;
+  ns_momentum_kernel<<<dim3(static_cast<unsigned>(nitems)), dim3(kThreads), 0, s>>>(mats, ns, items, beta);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_scale(hipStream_t s, NsDev* ns_dev, int32_t count, float eps) {
+  if (count <= 0) return hipSuccess;
+  ns_scale_kernel<<<dim3(count), dim3(kThreads), 0, s>>>(ns_dev, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_cast(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                          const TileItem* items, int64_t nitems, int prec) {
+  if (nitems <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(nitems)), block(kThreads);
+  if (prec == 0)
+    ns_cast_kernel<uint16_t><<<grid, block, 0, s>>>(mats, ns, items);
+  else
+    ns_cast_kernel<float><<<grid, block, 0, s>>>(mats, ns, items);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_gemm(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                          const GemmItem* items, int64_t nitems, int op, int tile, int prec,
+                          int iter, int last, float a, float b, float c, float wd) {
+  if (nitems <= 0) return hipSuccess;
+  if (prec == 0) {
+    if (tile == 256) return launch_gemm_t<uint16_t, 256>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
+    return launch_gemm_t<uint16_t, 128>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
+  }
+  if (tile == 256) return launch_gemm_t<float, 256>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
+  return launch_gemm_t<float, 128>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
+}
+
+}  // namespace muon

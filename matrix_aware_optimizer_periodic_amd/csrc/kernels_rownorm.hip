@@ -1,0 +1,272 @@
+// Non-refresh step: fused momentum + RowNorm + weight update.
+//
+// PaperDaily post on "Scaling Muon for Diffusion Transformers", section
+// "Periodic Row-wise Muon": on steps with t mod K != 0 the update direction
+// is gamma * RowNorm_eps(M) of the current momentum, where (blog fig. 4)
+// every row is divided by max(||row||_2, eps).  For tall matrices the slices
+// are columns: the post's section "distributed co-design", paper Eq. (8),
+// normalises them by column sums of squares over the rows.
+//
+// Both kernels are HBM-bound: per element they read G (2 or 4 B), M (4 B)
+// and W (4 B) and write M (4 B) and W (4 B).  Reductions run in a fixed
+// order, so results are bitwise reproducible from run to run.
+#include <hip/hip_runtime.h>
+
+#include "muon_internal.h"
+
+namespace muon {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Four consecutive gradient values starting at element idx (16-B aligned for
+// f32, 8-B aligned for bf16).
+__device__ __forceinline__ float4 load_g4(const void* g, int gdt, int64_t idx) {
+  if (gdt == 1) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g) + idx);
+    return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
+                       bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
+  }
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(g) + idx);
+}
+
+__device__ __forceinline__ float load_g1(const void* g, int gdt, int64_t idx) {
+  if (gdt == 1) return bf16_to_f32(static_cast<const uint16_t*>(g)[idx]);
+  return static_cast<const float*>(g)[idx];
+}
+
+__device__ __forceinline__ float4 fma4(float s, float4 a, float4 b) {  // s*a + b
+  return make_float4(fmaf(s, a.x, b.x), fmaf(s, a.y, b.y), fmaf(s, a.z, b.z), fmaf(s, a.w, b.w));
+}
+
+__device__ __forceinline__ float dot4(float4 a) {
+  return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+}
+
+// Sum over the 256-thread block in a fixed order; every thread gets the total.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__device__ __forceinline__ int find_mat(const int64_t* prefix, int nmat, int64_t gid) {
+  int lo = 0, hi = nmat - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= gid) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup per row.  MAXCH > 0: the row (<= MAXCH * 1024 elements)
+// stays in registers between the norm and the update.  MAXCH == 0: any
+// length, the updated momentum is re-read for the second pass.
+template <int MAXCH>
+__global__ __launch_bounds__(kThreads) void rownorm_rows_kernel(
+    const MatDev* __restrict__ mats, const int32_t* __restrict__ mat_ids,
+    const int64_t* __restrict__ row_prefix, int32_t nmat, StepScalars sc) {
+  __shared__ float red[4];
+  const int64_t gid = blockIdx.x;
+  const int k = find_mat(row_prefix, nmat, gid);
+  const MatDev d = mats[mat_ids[k]];
+  const int64_t row = gid - row_prefix[k];
+  const int64_t n = d.cols;
+  float* __restrict__ M = d.mom + row * n;
+  float* __restrict__ W = d.w + row * n;
+  const int64_t goff = row * n;
+  const int tid = threadIdx.x;
+  const float wkeep = 1.0f - sc.lr * sc.wd;
+  float ss = 0.f;
+
+  if ((n & 3) == 0) {
+    if constexpr (MAXCH > 0) {
+      float4 mv[MAXCH];
+#pragma unroll
+      for (int ch = 0; ch < MAXCH; ++ch) {
+        const int64_t e = (int64_t(ch) * kThreads + tid) * 4;
+        if (e < n) {
+          const float4 g = load_g4(d.g, d.gdt, goff + e);
+          const float4 m = *reinterpret_cast<const float4*>(M + e);
+          mv[ch] = fma4(sc.beta, m, g);
+          ss += dot4(mv[ch]);
+        }
+      }
+      const float tot = block_sum(ss, red);
+      const float coef = sc.lr * sc.gamma / fmaxf(sqrtf(tot), sc.eps_row);
+#pragma unroll
+      for (int ch = 0; ch < MAXCH; ++ch) {
+        const int64_t e = (int64_t(ch) * kThreads + tid) * 4;
+        if (e < n) {
+          *reinterpret_cast<float4*>(M + e) = mv[ch];
+          float4 w = *reinterpret_cast<const float4*>(W + e);
+          w = make_float4(w.x * wkeep, w.y * wkeep, w.z * wkeep, w.w * wkeep);
+          *reinterpret_cast<float4*>(W + e) = fma4(-coef, mv[ch], w);
+        }
+      }
+    } else {
+      for (int64_t e = int64_t(tid) * 4; e < n; e += kThreads * 4) {
+        const float4 g = load_g4(d.g, d.gdt, goff + e);
+        const float4 m = fma4(sc.beta, *reinterpret_cast<const float4*>(M + e), g);
+        *reinterpret_cast<float4*>(M + e) = m;
+        ss += dot4(m);
+      }
+      const float tot = block_sum(ss, red);
+      const float coef = sc.lr * sc.gamma / fmaxf(sqrtf(tot), sc.eps_row);
+      for (int64_t e = int64_t(tid) * 4; e < n; e += kThreads * 4) {
+        const float4 m = *reinterpret_cast<const float4*>(M + e);
+        float4 w = *reinterpret_cast<const float4*>(W + e);
+        w = make_float4(w.x * wkeep, w.y * wkeep, w.z * wkeep, w.w * wkeep);
+        *reinterpret_cast<float4*>(W + e) = fma4(-coef, m, w);
+      }
+    }
+  } else {
+    // Ragged row length: scalar, two passes.
+    for (int64_t e = tid; e < n; e += kThreads) {
+      const float m = fmaf(sc.beta, M[e], load_g1(d.g, d.gdt, goff + e));
+      M[e] = m;
+      ss += m * m;
+    }
+    const float tot = block_sum(ss, red);
+    const float coef = sc.lr * sc.gamma / fmaxf(sqrtf(tot), sc.eps_row);
+    for (int64_t e = tid; e < n; e += kThreads) W[e] = fmaf(-coef, M[e], W[e] * wkeep);
+  }
+}
+
+// Tall matrices, slices = columns.  A tile is kColTileRows x kColTileCols;
+// thread (rg = tid / 64, ct = tid % 64) owns 4 columns and rows rg, rg+4, ...
+// Phase 1 writes the new momentum and one partial column sum of squares per
+// (row tile, column); phase 2 adds the partials of all row tiles in order,
+// then scales and updates W.
+template <int PHASE>
+__global__ __launch_bounds__(kThreads) void rownorm_cols_kernel(
+    const MatDev* __restrict__ mats, const TileItem* __restrict__ tiles, StepScalars sc) {
+  __shared__ float red[4][kColTileCols];
+  const TileItem it = tiles[blockIdx.x];
+  const MatDev d = mats[it.id];
+  const int64_t m = d.rows, n = d.cols;
+  const int64_t r0 = int64_t(it.ti) * kColTileRows;
+  const int64_t r1 = min(m, r0 + kColTileRows);
+  const int64_t c0 = int64_t(it.tj) * kColTileCols;
+  const int rg = threadIdx.x >> 6, ct = threadIdx.x & 63;
+  const bool vec = (n & 3) == 0;
+  // local column offsets owned by this thread (vector: 4 adjacent; scalar: strided)
+  int lc[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) lc[v] = vec ? ct * 4 + v : ct + 64 * v;
+  const int64_t nchunk = (m + kColTileRows - 1) / kColTileRows;
+
+  if constexpr (PHASE == 1) {
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    if (vec) {
+      const int64_t col = c0 + ct * 4;
+      if (col < n) {
+        for (int64_t r = r0 + rg; r < r1; r += 4) {
+          const int64_t e = r * n + col;
+          const float4 g = load_g4(d.g, d.gdt, e);
+          const float4 mm = fma4(sc.beta, *reinterpret_cast<const float4*>(d.mom + e), g);
+          *reinterpret_cast<float4*>(d.mom + e) = mm;
+          ss[0] += mm.x * mm.x; ss[1] += mm.y * mm.y; ss[2] += mm.z * mm.z; ss[3] += mm.w * mm.w;
+        }
+      }
+    } else {
+      for (int64_t r = r0 + rg; r < r1; r += 4) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t col = c0 + lc[v];
+          if (col < n) {
+            const int64_t e = r * n + col;
+            const float mm = fmaf(sc.beta, d.mom[e], load_g1(d.g, d.gdt, e));
+            d.mom[e] = mm;
+            ss[v] += mm * mm;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[rg][lc[v]] = ss[v];
+    __syncthreads();
+    if (rg == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t col = c0 + lc[v];
+        if (col < n)
+          d.part[int64_t(it.ti) * n + col] =
+              (red[0][lc[v]] + red[1][lc[v]]) + (red[2][lc[v]] + red[3][lc[v]]);
+      }
+    }
+  } else {
+    float coef[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t col = c0 + lc[v];
+      float s = 0.f;
+      if (col < n)
+        for (int64_t k = 0; k < nchunk; ++k) s += d.part[k * n + col];
+      coef[v] = sc.lr * sc.gamma / fmaxf(sqrtf(s), sc.eps_row);
+    }
+    const float wkeep = 1.0f - sc.lr * sc.wd;
+    if (vec) {
+      const int64_t col = c0 + ct * 4;
+      if (col < n) {
+        for (int64_t r = r0 + rg; r < r1; r += 4) {
+          const int64_t e = r * n + col;
+          const float4 mm = *reinterpret_cast<const float4*>(d.mom + e);
+          const float4 w = *reinterpret_cast<const float4*>(d.w + e);
+          *reinterpret_cast<float4*>(d.w + e) =
+              make_float4(fmaf(-coef[0], mm.x, w.x * wkeep), fmaf(-coef[1], mm.y, w.y * wkeep),
+                          fmaf(-coef[2], mm.z, w.z * wkeep), fmaf(-coef[3], mm.w, w.w * wkeep));
+        }
+      }
+    } else {
+      for (int64_t r = r0 + rg; r < r1; r += 4) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t col = c0 + lc[v];
+          if (col < n) {
+            const int64_t e = r * n + col;
+            d.w[e] = fmaf(-coef[v], d.mom[e], d.w[e] * wkeep);
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rownorm_rows(hipStream_t s, const MatDev* mats, const int32_t* mat_ids,
+                               const int64_t* row_prefix, int32_t nmat, int64_t total_rows,
+                               int max_chunks, StepScalars sc) {
+  if (total_rows <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(total_rows)), block(kThreads);
+  switch (max_chunks) {
+    case 1: rownorm_rows_kernel<1><<<grid, block, 0, s>>>(mats, mat_ids, row_prefix, nmat, sc); break;
+    case 2: rownorm_rows_kernel<2><<<grid, block, 0, s>>>(mats, mat_ids, row_prefix, nmat, sc); break;
+    case 4: rownorm_rows_kernel<4><<<grid, block, 0, s>>>(mats, mat_ids, row_prefix, nmat, sc); break;
+    case 8: rownorm_rows_kernel<8><<<grid, block, 0, s>>>(mats, mat_ids, row_prefix, nmat, sc); break;
+    case 16: rownorm_rows_kernel<16><<<grid, block, 0, s>>>(mats, mat_ids, row_prefix, nmat, sc); break;
+    case 32: rownorm_rows_kernel<32><<<grid, block, 0, s>>>(mats, mat_ids, row_prefix, nmat, sc); break;
+    default: rownorm_rows_kernel<0><<<grid, block, 0, s>>>(mats, mat_ids, row_prefix, nmat, sc); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem* tiles,
+                               int64_t ntiles, int phase, StepScalars sc) {
+  if (ntiles <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(ntiles)), block(kThreads);
+  if (phase == 1)
+    rownorm_cols_kernel<1><<<grid, block, 0, s>>>(mats, tiles, sc);
+  else
+    rownorm_cols_kernel<2><<<grid, block, 0, s>>>(mats, tiles, sc);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,124 @@
+// Internal structures shared by the host planner and the gfx950 kernels.
+//
+// Every table here lives in the caller's state buffer; the planner fills
+// host copies and uploads them once in muon_init.  Pointers to the caller's
+// W / G tensors are patched by a small kernel when a step passes new ones.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace muon {
+
+// One Muon weight.
+struct MatDev {
+  float* w;          // stored W, rows x cols, row-major (caller-owned)
+  const void* g;     // gradient, same shape (caller-owned), dtype = gdt
+  float* mom;        // momentum, rows x cols fp32 (state buffer)
+  int64_t rows, cols;
+  float* part;       // RowNorm column partial sums (tall kernel), nchunk x cols
+  int32_t gdt;       // 0 = f32, 1 = bf16
+  int32_t pad;
+};
+
+// One AdamW tensor (flattened).
+struct AdamDev {
+  float* p;
+  const void* g;
+  float* m;
+  float* v;
+  int64_t numel;
+  int32_t gdt;
+  int32_t pad;
+};
+
+// A contiguous piece of one AdamW tensor handled by one workgroup.
+struct AdamChunk {
+  int32_t tensor;
+  int32_t len;
+  int64_t off;
+};
+
+// One Newton-Schulz problem: a whole matrix, or one MuonBP column block.
+// X orientation is wide: r = min(rows, cols) rows, c = max columns.  The
+// stored block (rows x cols at column col0 of a row-major matrix with row
+// stride ld) equals X when wide and X^T when tall.
+struct NsDev {
+  int32_t mat;       // MatDev index
+  int32_t tall;      // stored block is c x r
+  int64_t rows, cols, col0, ld;
+  int64_t r, c, rp, cp;   // logical and padded X dims
+  void* xr;          // rp x cp, X row-major              (T = bf16 or f32)
+  void* xc[2];       // cp x rp, X^T row-major, ping-pong
+  void* a;           // rp x rp, X X^T
+  void* b;           // rp x rp, b A + c A A
+  float* part;       // Frobenius partial sums, nparts
+  float* scale;      // 1 / (||M||_F + eps), one float
+  float* adiag;      // rp: diagonal of A kept in fp32
+  float* bdiag;      // rp: diagonal of B kept in fp32 (stored B has 0 there)
+  int32_t nparts;
+  int32_t rows_per_part;
+  float lr;          // learning rate applied by the final product
+  float pad;
+};
+
+// A GEMM output tile of one NsDev.
+struct GemmItem {
+  int32_t ns;
+  int16_t ti, tj;
+};
+
+// A prep tile of one NsDev (64 x 64 in stored coordinates of the padded
+// block) or a RowNorm tile of one matrix.
+struct TileItem {
+  int32_t id;
+  int16_t ti, tj;
+};
+
+// Pointer patch applied when a step passes new W / G pointers.
+constexpr int kPatchMax = 24;
+struct PatchArgs {
+  int32_t count;
+  int32_t adam;           // 0: MatDev table, 1: AdamDev table
+  int32_t idx[kPatchMax];
+  void* w[kPatchMax];
+  const void* g[kPatchMax];
+};
+
+struct StepScalars {
+  float lr, beta, gamma, eps_row, wd;
+};
+
+// ---- launchers (kernels_*.hip); all return hipGetLastError() -------------
+// Rows of the matrices mat_ids[0..nmat) (one workgroup per row); row_prefix
+// has nmat + 1 entries.  Every row must have <= max_chunks * kRowChunkElems
+// elements, or max_chunks == 0 selects the streaming two-pass variant.
+hipError_t launch_rownorm_rows(hipStream_t s, const MatDev* mats, const int32_t* mat_ids,
+                               const int64_t* row_prefix, int32_t nmat, int64_t total_rows,
+                               int max_chunks, StepScalars sc);
+// Column-normalised (tall) matrices, phase 1 (momentum + column partials) or
+// phase 2 (norms + weight update), one workgroup per tile.
+hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem* tiles,
+                               int64_t ntiles, int phase, StepScalars sc);
+hipError_t launch_ns_momentum(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                              const TileItem* items, int64_t nitems, float beta);
+hipError_t launch_ns_scale(hipStream_t s, NsDev* ns_dev, int32_t count, float eps);
+hipError_t launch_ns_cast(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                          const TileItem* items, int64_t nitems, int prec);
+hipError_t launch_ns_gemm(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                          const GemmItem* items, int64_t nitems, int op, int tile,
+                          int prec, int iter, int last, float a, float b, float c, float wd);
+hipError_t launch_adamw(hipStream_t s, const AdamDev* t, const AdamChunk* chunks,
+                        int64_t nchunks, float lr, float b1, float b2, float eps,
+                        float wd, float bc1, float bc2);
+hipError_t launch_patch(hipStream_t s, MatDev* mats, AdamDev* adams, const PatchArgs& args);
+
+constexpr int kGemmGram = 0, kGemmPoly = 1, kGemmProduct = 2;
+constexpr int kRowChunkElems = 1024;   // elements per row-kernel chunk (256 thr x 4)
+constexpr int kColTileRows = 512;      // tall RowNorm tile rows
+constexpr int kColTileCols = 256;      // tall RowNorm tile columns
+constexpr int kPrepTile = 64;          // NS5 cast/transpose tile
+constexpr int kMomRowsPerPart = 8;     // rows per Frobenius partial
+constexpr int kAdamChunk = 4096;       // elements per AdamW workgroup
+
+}  // namespace muon

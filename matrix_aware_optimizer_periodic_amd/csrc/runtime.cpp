@@ -1,0 +1,821 @@
+// Host side of the C ABI: validation, planning, state-buffer carving, and the
+// per-step launch sequence.  No device memory is ever allocated here: every
+// device byte comes from the caller's state buffer.
+//
+// Schedule (PaperDaily post on "Scaling Muon for Diffusion Transformers",
+// section "Periodic Row-wise Muon", blog fig. 3): refresh when t mod K == 0,
+// RowNorm otherwise; with MuonBP ("MuonBP: Faster Muon via Block-Periodic
+// Orthogonalization", abstract) full NS5 every bp_period steps and per-block
+// NS5 in between, with its own step size.
+//
+// The pages' distributed design gathers momentum in buckets so only a
+// bounded number of full matrices is materialised at a time (the post's
+// section "distributed co-design").  On one GPU that becomes NS5 "chunks":
+// problems are grouped so that one chunk's workspace stays under
+// ns_workspace_max, and each chunk runs all its matrices through every
+// Newton-Schulz round with one grouped launch per product.
+#include "../../include/muon.h"
+#include "muon_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct RowGroup {
+  int max_chunks = 0;
+  std::vector<int32_t> ids;
+  std::vector<int64_t> prefix;
+  size_t off_ids = 0, off_prefix = 0;
+};
+
+struct GemmList {
+  std::vector<GemmItem> items;
+  size_t off = 0;
+};
+
+struct NsChunk {
+  std::vector<NsDev> ns;          // device pointers filled once base is known
+  std::vector<size_t> ws_off;     // per problem: workspace offset (relative to ws base)
+  std::vector<TileItem> mom_items, cast_items;
+  GemmList gemm[3][2];            // [op][tile == 256]
+  size_t off_ns = 0, off_mom = 0, off_cast = 0;
+  size_t ws_bytes = 0;
+};
+
+struct Plan {
+  // per parameter
+  std::vector<int32_t> table_index;      // index into mats or adams
+  std::vector<MatDev> mats;
+  std::vector<AdamDev> adams;
+  std::vector<size_t> mom_off, part_off, m_off, v_off;
+  std::vector<RowGroup> row_groups;
+  std::vector<TileItem> col_tiles;
+  std::vector<AdamChunk> adam_chunks;
+  std::vector<NsChunk> ns_full, ns_block;
+  size_t off_mats = 0, off_adams = 0, off_col_tiles = 0, off_adam_chunks = 0;
+  size_t ws_base = 0, ws_bytes = 0;
+  size_t zero_end = 0;                    // bytes [0, zero_end) are zeroed at init
+  size_t total = 0;
+};
+
+struct Bump {
+  size_t cur = 0;
+  size_t take(size_t bytes) {
+    const size_t o = cur;
+    cur = align_up(cur + bytes, kAlign);
+    return o;
+  }
+};
+
+bool finite(float x) { return std::isfinite(x); }
+
+muon_status check_config(const muon_config* c, std::string& err) {
+  if (!c) { err = "config is NULL"; return MUON_E_ARG; }
+  if (c->K < 1) { err = "K must be >= 1"; return MUON_E_ARG; }
+  if (c->ns_iters < 1 || c->ns_iters > 64) { err = "ns_iters must be in [1, 64]"; return MUON_E_ARG; }
+  if (!finite(c->lr) || !finite(c->beta) || !finite(c->gamma) || !finite(c->ns_a) ||
+      !finite(c->ns_b) || !finite(c->ns_c) || !finite(c->muon_wd) || !finite(c->adam_lr) ||
+      !finite(c->adam_wd) || !finite(c->bp_lr_ratio)) {
+    err = "non-finite config value"; return MUON_E_ARG;
+  }
+  if (!(c->eps_row >= 0.f) || !(c->ns_eps >= 0.f) || !(c->adam_eps >= 0.f)) {
+    err = "eps values must be >= 0"; return MUON_E_ARG;
+  }
+  if (c->ns_precision != MUON_NS_BF16 && c->ns_precision != MUON_NS_F32) {
+    err = "ns_precision must be MUON_NS_BF16 or MUON_NS_F32"; return MUON_E_ARG;
+  }
+  if (c->rownorm_axis != 0 && c->rownorm_axis != 1) { err = "rownorm_axis must be 0 or 1"; return MUON_E_ARG; }
+  if (c->bp_blocks < 0) { err = "bp_blocks must be >= 0"; return MUON_E_ARG; }
+  if (c->bp_blocks > 0 && c->bp_period < 1) { err = "bp_period must be >= 1"; return MUON_E_ARG; }
+  if (!(c->adam_b1 >= 0.f && c->adam_b1 < 1.f) || !(c->adam_b2 >= 0.f && c->adam_b2 < 1.f)) {
+    err = "adam betas must be in [0, 1)"; return MUON_E_ARG;
+  }
+  return MUON_OK;
+}
+
+muon_status check_tensor(const muon_tensor& t, bool need_f32, const char* what, int32_t i,
+                         std::string& err) {
+  char buf[160];
+  if (t.rows < 1 || t.cols < 1 || t.ld != t.cols || t.reserved != 0) {
+    snprintf(buf, sizeof buf, "%s %d: need rows, cols >= 1, ld == cols, reserved == 0", what, i);
+    err = buf;
+    return (t.ld != t.cols && t.rows >= 1 && t.cols >= 1) ? MUON_E_ALIGN : MUON_E_SHAPE;
+  }
+  if (t.rows > (int64_t(1) << 40) / t.cols) {
+    snprintf(buf, sizeof buf, "%s %d: tensor too large", what, i); err = buf; return MUON_E_SHAPE;
+  }
+  if (t.dtype != MUON_F32 && t.dtype != MUON_BF16) {
+    snprintf(buf, sizeof buf, "%s %d: unknown dtype %d", what, i, t.dtype); err = buf; return MUON_E_DTYPE;
+  }
+  if (need_f32 && t.dtype != MUON_F32) {
+    snprintf(buf, sizeof buf, "%s %d: must be F32", what, i); err = buf; return MUON_E_DTYPE;
+  }
+  return MUON_OK;
+}
+
+muon_status check_ptr(const void* p, const char* what, int32_t i, std::string& err) {
+  char buf[128];
+  if (!p) { snprintf(buf, sizeof buf, "%s %d: NULL pointer", what, i); err = buf; return MUON_E_ARG; }
+  if (reinterpret_cast<uintptr_t>(p) % 16) {
+    snprintf(buf, sizeof buf, "%s %d: pointer not 16-byte aligned", what, i); err = buf; return MUON_E_ALIGN;
+  }
+  return MUON_OK;
+}
+
+int row_chunk_class(int64_t cols) {
+  if (cols % 4) return 0;
+  const int64_t need = ceil_div(cols, kRowChunkElems);
+  for (int c : {1, 2, 4, 8, 16, 32})
+    if (need <= c) return c;
+  return 0;
+}
+
+// Reorder a natural-order work list so the hardware's round-robin dispatch
+// (workgroup i -> XCD i mod 8) gives each XCD one contiguous segment of it:
+// neighbouring tiles, which share operand panels, then meet in the same L2.
+template <typename T>
+void xcd_interleave(std::vector<T>& v) {
+  const int64_t n = static_cast<int64_t>(v.size());
+  if (n < 16) return;
+  const int64_t q = n / 8, rem = n % 8;
+  std::vector<T> out;
+  out.reserve(v.size());
+  for (int64_t local = 0; local <= q; ++local)
+    for (int64_t x = 0; x < 8; ++x) {
+      const int64_t size = q + (x < rem ? 1 : 0);
+      if (local < size) out.push_back(v[x * q + std::min<int64_t>(x, rem) + local]);
+    }
+  v.swap(out);
+}
+
+// One NS problem (a whole matrix or one MuonBP block).
+struct Problem {
+  int32_t mat;
+  int64_t rows, cols, col0, ld;
+  float lr;
+};
+
+size_t problem_ws_bytes(const Problem& p, int tile, size_t es, int64_t* rp_out, int64_t* cp_out,
+                        int32_t* nparts_out) {
+  const int64_t r = std::min(p.rows, p.cols), c = std::max(p.rows, p.cols);
+  const int64_t rp = ceil_div(r, tile) * tile, cp = ceil_div(c, tile) * tile;
+  const int32_t nparts = static_cast<int32_t>(ceil_div(p.rows, kMomRowsPerPart));
+  *rp_out = rp; *cp_out = cp; *nparts_out = nparts;
+  size_t b = 0;
+  b += align_up(size_t(rp) * cp * es, kAlign);          // xr
+  b += 2 * align_up(size_t(cp) * rp * es, kAlign);      // xc[0], xc[1]
+  b += 2 * align_up(size_t(rp) * rp * es, kAlign);      // a, b
+  b += align_up(size_t(nparts) * 4, kAlign);            // partials
+  b += kAlign;                                          // scale
+  b += 2 * align_up(size_t(rp) * 4, kAlign);            // adiag, bdiag
+  return b;
+}
+
+int tile_for(int64_t r) { return r >= 1024 ? 256 : 128; }
+
+std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_config& cfg) {
+  const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
+  std::vector<NsChunk> chunks;
+  NsChunk cur;
+  for (const Problem& p : probs) {
+    int64_t rp, cp;
+    int32_t nparts;
+    const int64_t r = std::min(p.rows, p.cols);
+    const int tile = tile_for(r);
+    const size_t wb = problem_ws_bytes(p, tile, es, &rp, &cp, &nparts);
+    if (!cur.ns.empty() && cfg.ns_workspace_max && cur.ws_bytes + wb > cfg.ns_workspace_max) {
+      chunks.push_back(std::move(cur));
+      cur = NsChunk();
+    }
+    NsDev d{};
+    d.mat = p.mat;
+    d.tall = p.rows > p.cols ? 1 : 0;
+    d.rows = p.rows; d.cols = p.cols; d.col0 = p.col0; d.ld = p.ld;
+    d.r = r; d.c = std::max(p.rows, p.cols); d.rp = rp; d.cp = cp;
+    d.nparts = nparts;
+    d.rows_per_part = kMomRowsPerPart;
+    d.lr = p.lr;
+    cur.ws_off.push_back(cur.ws_bytes);
+    cur.ws_bytes += wb;
+    cur.ns.push_back(d);
+  }
+  if (!cur.ns.empty()) chunks.push_back(std::move(cur));
+
+  for (NsChunk& ch : chunks) {
+    for (int32_t k = 0; k < static_cast<int32_t>(ch.ns.size()); ++k) {
+      const NsDev& d = ch.ns[k];
+      const int tile = tile_for(d.r);
+      const int t256 = tile == 256 ? 1 : 0;
+      for (int32_t q = 0; q < d.nparts; ++q) ch.mom_items.push_back(TileItem{k, int16_t(q), 0});
+      const int64_t sp = d.tall ? d.cp : d.rp, sq = d.tall ? d.rp : d.cp;
+      for (int64_t a = 0; a < sp / kPrepTile; ++a)
+        for (int64_t b = 0; b < sq / kPrepTile; ++b)
+          ch.cast_items.push_back(TileItem{k, int16_t(a), int16_t(b)});
+      const int64_t nr = d.rp / tile, nc = d.cp / tile;
+      for (int64_t i = 0; i < nr; ++i)
+        for (int64_t j = i; j < nr; ++j) {
+          ch.gemm[kGemmGram][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+          ch.gemm[kGemmPoly][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+        }
+      for (int64_t i = 0; i < nr; ++i)
+        for (int64_t j = 0; j < nc; ++j)
+          ch.gemm[kGemmProduct][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+    }
+    for (auto& op : ch.gemm)
+      for (auto& gl : op) xcd_interleave(gl.items);
+  }
+  return chunks;
+}
+
+muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const int32_t* kinds,
+                       int32_t n, char* base, Plan& pl, std::string& err) {
+  pl = Plan();
+  Bump bump;
+  pl.table_index.assign(n, -1);
+  pl.mom_off.assign(n, 0); pl.part_off.assign(n, 0); pl.m_off.assign(n, 0); pl.v_off.assign(n, 0);
+  // 1. optimizer state (zeroed at init)
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_tensor& t = params[i];
+    const size_t numel = size_t(t.rows) * size_t(t.cols);
+    if (kinds[i] == MUON_KIND_MATRIX) {
+      pl.table_index[i] = static_cast<int32_t>(pl.mats.size());
+      pl.mom_off[i] = bump.take(numel * 4);
+      MatDev d{};
+      d.rows = t.rows; d.cols = t.cols;
+      pl.mats.push_back(d);
+    } else {
+      pl.table_index[i] = static_cast<int32_t>(pl.adams.size());
+      pl.m_off[i] = bump.take(numel * 4);
+      pl.v_off[i] = bump.take(numel * 4);
+      AdamDev a{};
+      a.numel = int64_t(numel);
+      pl.adams.push_back(a);
+    }
+  }
+  pl.zero_end = bump.cur;
+  // 2. RowNorm plan
+  const bool cols_mode = cfg.rownorm_axis == 0;
+  std::vector<RowGroup> groups(7);
+  const int classes[7] = {0, 1, 2, 4, 8, 16, 32};
+  for (int g = 0; g < 7; ++g) groups[g].max_chunks = classes[g];
+  for (int32_t i = 0; i < n; ++i) {
+    if (kinds[i] != MUON_KIND_MATRIX) continue;
+    const muon_tensor& t = params[i];
+    const int32_t mi = pl.table_index[i];
+    if (cols_mode && t.rows > t.cols) {
+      const int64_t nchunk = ceil_div(t.rows, kColTileRows);
+      if (nchunk > 32767 || ceil_div(t.cols, kColTileCols) > 32767) {
+        err = "param " + std::to_string(i) + ": too large for the tile index range";
+        return MUON_E_SHAPE;
+      }
+      pl.part_off[i] = bump.take(size_t(nchunk) * t.cols * 4);
+      for (int64_t a = 0; a < nchunk; ++a)
+        for (int64_t b = 0; b < ceil_div(t.cols, kColTileCols); ++b)
+          pl.col_tiles.push_back(TileItem{mi, int16_t(a), int16_t(b)});
+    } else {
+      const int cls = row_chunk_class(t.cols);
+      RowGroup& g = groups[std::find(classes, classes + 7, cls) - classes];
+      if (g.prefix.empty()) g.prefix.push_back(0);
+      g.ids.push_back(mi);
+      g.prefix.push_back(g.prefix.back() + t.rows);
+    }
+  }
+  for (RowGroup& g : groups)
+    if (!g.ids.empty()) pl.row_groups.push_back(std::move(g));
+  // 3. AdamW chunks
+  for (int32_t i = 0; i < n; ++i) {
+    if (kinds[i] != MUON_KIND_ADAMW) continue;
+    const int64_t numel = params[i].rows * params[i].cols;
+    for (int64_t o = 0; o < numel; o += kAdamChunk)
+      pl.adam_chunks.push_back(AdamChunk{pl.table_index[i],
+                                         int32_t(std::min<int64_t>(kAdamChunk, numel - o)), o});
+  }
+  // 4. NS plans
+  std::vector<Problem> full, block;
+  for (int32_t i = 0; i < n; ++i) {
+    if (kinds[i] != MUON_KIND_MATRIX) continue;
+    const muon_tensor& t = params[i];
+    full.push_back(Problem{pl.table_index[i], t.rows, t.cols, 0, t.cols, cfg.lr});
+    if (cfg.bp_blocks > 0) {
+      if (t.cols % cfg.bp_blocks) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "param %d: %lld columns do not split into %d MuonBP blocks", i,
+                 (long long)t.cols, cfg.bp_blocks);
+        err = buf;
+        return MUON_E_SHAPE;
+      }
+      const int64_t w = t.cols / cfg.bp_blocks;
+      for (int32_t b = 0; b < cfg.bp_blocks; ++b)
+        block.push_back(Problem{pl.table_index[i], t.rows, w, b * w, t.cols, cfg.lr * cfg.bp_lr_ratio});
+    }
+  }
+  pl.ns_full = plan_ns(full, cfg);
+  pl.ns_block = plan_ns(block, cfg);
+  for (auto* plan : {&pl.ns_full, &pl.ns_block})
+    for (NsChunk& ch : *plan)
+      for (const NsDev& d : ch.ns)
+        if (d.rp / 128 > 32767 || d.cp / 64 > 32767 || d.nparts > 32767) {
+          err = "matrix too large for the tile index range"; return MUON_E_SHAPE;
+        }
+  // 5. tables
+  pl.off_mats = bump.take(pl.mats.size() * sizeof(MatDev));
+  pl.off_adams = bump.take(pl.adams.size() * sizeof(AdamDev));
+  pl.off_col_tiles = bump.take(pl.col_tiles.size() * sizeof(TileItem));
+  pl.off_adam_chunks = bump.take(pl.adam_chunks.size() * sizeof(AdamChunk));
+  for (RowGroup& g : pl.row_groups) {
+    g.off_ids = bump.take(g.ids.size() * 4);
+    g.off_prefix = bump.take(g.prefix.size() * 8);
+  }
+  size_t ws = 0;
+  for (auto* plan : {&pl.ns_full, &pl.ns_block})
+    for (NsChunk& ch : *plan) {
+      ch.off_ns = bump.take(ch.ns.size() * sizeof(NsDev));
+      ch.off_mom = bump.take(ch.mom_items.size() * sizeof(TileItem));
+      ch.off_cast = bump.take(ch.cast_items.size() * sizeof(TileItem));
+      for (auto& op : ch.gemm)
+        for (auto& gl : op) gl.off = bump.take(gl.items.size() * sizeof(GemmItem));
+      ws = std::max(ws, ch.ws_bytes);
+    }
+  // 6. NS workspace, shared by all chunks of both plans
+  pl.ws_base = bump.take(ws);
+  pl.ws_bytes = ws;
+  pl.total = bump.cur;
+
+  // Device pointers (meaningful only when base is the real buffer).
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t k = pl.table_index[i];
+    if (kinds[i] == MUON_KIND_MATRIX) {
+      MatDev& d = pl.mats[k];
+      d.mom = static_cast<float*>(at(pl.mom_off[i]));
+      d.part = static_cast<float*>(at(pl.part_off[i]));
+    } else {
+      AdamDev& a = pl.adams[k];
+      a.m = static_cast<float*>(at(pl.m_off[i]));
+      a.v = static_cast<float*>(at(pl.v_off[i]));
+    }
+  }
+  const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
+  for (auto* plan : {&pl.ns_full, &pl.ns_block})
+    for (NsChunk& ch : *plan)
+      for (size_t k = 0; k < ch.ns.size(); ++k) {
+        NsDev& d = ch.ns[k];
+        size_t o = pl.ws_base + ch.ws_off[k];
+        d.xr = at(o); o += align_up(size_t(d.rp) * d.cp * es, kAlign);
+        d.xc[0] = at(o); o += align_up(size_t(d.cp) * d.rp * es, kAlign);
+        d.xc[1] = at(o); o += align_up(size_t(d.cp) * d.rp * es, kAlign);
+        d.a = at(o); o += align_up(size_t(d.rp) * d.rp * es, kAlign);
+        d.b = at(o); o += align_up(size_t(d.rp) * d.rp * es, kAlign);
+        d.part = static_cast<float*>(at(o)); o += align_up(size_t(d.nparts) * 4, kAlign);
+        d.scale = static_cast<float*>(at(o)); o += kAlign;
+        d.adiag = static_cast<float*>(at(o)); o += align_up(size_t(d.rp) * 4, kAlign);
+        d.bdiag = static_cast<float*>(at(o));
+      }
+  return MUON_OK;
+}
+
+muon_status validate_list(const muon_config* cfg, const muon_tensor* params,
+                          const muon_tensor* grads, const int32_t* kinds, int32_t n,
+                          bool check_ptrs, std::string& err) {
+  muon_status st = check_config(cfg, err);
+  if (st != MUON_OK) return st;
+  if (n < 0) { err = "n must be >= 0"; return MUON_E_ARG; }
+  if (n > 0 && (!params || !kinds)) { err = "params/kinds is NULL"; return MUON_E_ARG; }
+  if (n > 0 && check_ptrs && !grads) { err = "grads is NULL"; return MUON_E_ARG; }
+  for (int32_t i = 0; i < n; ++i) {
+    if (kinds[i] != MUON_KIND_MATRIX && kinds[i] != MUON_KIND_ADAMW) {
+      err = "param " + std::to_string(i) + ": unknown kind";
+      return MUON_E_ARG;
+    }
+    st = check_tensor(params[i], true, "param", i, err);
+    if (st != MUON_OK) return st;
+    if (check_ptrs) {
+      st = check_tensor(grads[i], false, "grad", i, err);
+      if (st != MUON_OK) return st;
+      if (grads[i].rows != params[i].rows || grads[i].cols != params[i].cols) {
+        err = "grad " + std::to_string(i) + ": shape differs from its param";
+        return MUON_E_SHAPE;
+      }
+      if ((st = check_ptr(params[i].ptr, "param", i, err)) != MUON_OK) return st;
+      if ((st = check_ptr(grads[i].ptr, "grad", i, err)) != MUON_OK) return st;
+    }
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+
+struct muon_ctx {
+  muon_config cfg{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  char* base = nullptr;
+  int32_t n = 0;
+  std::vector<muon_tensor> params, grads;  // init-time descriptors + current pointers
+  std::vector<int32_t> kinds;
+  Plan plan;
+  std::string err;
+  bool broken = false;
+  // measurement hook
+  bool timing = false;
+  std::vector<hipEvent_t> events;            // pool, two per recorded launch
+  std::vector<int32_t> event_class;          // class of each recorded pair
+  size_t events_used = 0;                    // pairs recorded since last read
+  ~muon_ctx() {
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+  }
+};
+
+namespace {
+
+muon_status hip_fail(muon_ctx* ctx, hipError_t e, const char* what) {
+  char buf[256];
+  snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
+  ctx->err = buf;
+  return MUON_E_HIP;
+}
+
+template <typename T>
+hipError_t upload(muon_ctx* ctx, size_t off, const std::vector<T>& v) {
+  if (v.empty()) return hipSuccess;
+  return hipMemcpyAsync(ctx->base + off, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice,
+                        ctx->stream);
+}
+
+// Records a start event for kernel class cls when timing is on; close()
+// records the stop event after the launch.
+struct Timed {
+  muon_ctx* ctx;
+  size_t pair = SIZE_MAX;
+  Timed(muon_ctx* c, int32_t cls) : ctx(c) {
+    if (!ctx->timing) return;
+    if (ctx->events.size() < 2 * (ctx->events_used + 1)) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      ctx->events.push_back(a);
+      ctx->events.push_back(b);
+      ctx->event_class.push_back(cls);
+    }
+    pair = ctx->events_used++;
+    ctx->event_class[pair] = cls;
+    (void)hipEventRecord(ctx->events[2 * pair], ctx->stream);
+  }
+  hipError_t close(hipError_t e) {
+    if (pair != SIZE_MAX) (void)hipEventRecord(ctx->events[2 * pair + 1], ctx->stream);
+    return e;
+  }
+};
+
+#define MUON_TIMED(ctx, cls, expr) Timed((ctx), (cls)).close(expr)
+
+#define MUON_HIP(ctx, expr)                                   \
+  do {                                                        \
+    const hipError_t e_ = (expr);                             \
+    if (e_ != hipSuccess) return hip_fail((ctx), e_, #expr);  \
+  } while (0)
+
+muon_status run_ns(muon_ctx* ctx, std::vector<NsChunk>& chunks) {
+  const muon_config& c = ctx->cfg;
+  const Plan& pl = ctx->plan;
+  const MatDev* mats = reinterpret_cast<const MatDev*>(ctx->base + pl.off_mats);
+  const int prec = c.ns_precision == MUON_NS_BF16 ? 0 : 1;
+  for (NsChunk& ch : chunks) {
+    NsDev* ns = reinterpret_cast<NsDev*>(ctx->base + ch.off_ns);
+    const TileItem* mom = reinterpret_cast<const TileItem*>(ctx->base + ch.off_mom);
+    const TileItem* cast = reinterpret_cast<const TileItem*>(ctx->base + ch.off_cast);
+    MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_MOMENTUM,
+                             launch_ns_momentum(ctx->stream, mats, ns, mom,
+                                                int64_t(ch.mom_items.size()), c.beta)));
+    MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_SCALE,
+                             launch_ns_scale(ctx->stream, ns, int32_t(ch.ns.size()), c.ns_eps)));
+    MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_CAST,
+                             launch_ns_cast(ctx->stream, mats, ns, cast,
+                                            int64_t(ch.cast_items.size()), prec)));
+    for (int it = 0; it < c.ns_iters; ++it) {
+      const int last = it == c.ns_iters - 1;
+      for (int op = 0; op < 3; ++op)
+        for (int t = 0; t < 2; ++t) {
+          const GemmList& gl = ch.gemm[op][t];
+          if (gl.items.empty()) continue;
+          const GemmItem* items = reinterpret_cast<const GemmItem*>(ctx->base + gl.off);
+          MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_GRAM + op,
+                                   launch_ns_gemm(ctx->stream, mats, ns, items,
+                                                  int64_t(gl.items.size()), op, t ? 256 : 128,
+                                                  prec, it, last, c.ns_a, c.ns_b, c.ns_c,
+                                                  c.muon_wd)));
+        }
+    }
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_config_default(muon_config* out) {
+  if (!out) return MUON_E_ARG;
+  std::memset(out, 0, sizeof *out);
+  out->lr = 0.02f;
+  out->beta = 0.95f;
+  out->gamma = 0.15f;
+  out->eps_row = 1e-8f;
+  out->K = 3;
+  out->ns_iters = 5;
+  out->ns_a = 3.4445f;
+  out->ns_b = -4.7750f;
+  out->ns_c = 2.0315f;
+  out->ns_eps = 1e-7f;
+  out->ns_precision = MUON_NS_BF16;
+  out->rownorm_axis = 0;
+  out->bp_blocks = 0;
+  out->bp_period = 3;
+  out->bp_lr_ratio = 0.5f;
+  out->muon_wd = 0.f;
+  out->adam_lr = 1e-3f;
+  out->adam_b1 = 0.9f;
+  out->adam_b2 = 0.999f;
+  out->adam_eps = 1e-8f;
+  out->adam_wd = 0.f;
+  out->ns_workspace_max = uint64_t(16) << 30;
+  return MUON_OK;
+}
+
+muon_status muon_state_bytes(const muon_config* cfg, const muon_tensor* params,
+                             const int32_t* kinds, int32_t n, size_t* bytes) {
+  std::string err;
+  if (!bytes) { g_last_error = "bytes is NULL"; return MUON_E_ARG; }
+  muon_status st = validate_list(cfg, params, nullptr, kinds, n, false, err);
+  if (st != MUON_OK) { g_last_error = err; return st; }
+  Plan pl;
+  st = build_plan(*cfg, params, kinds, n, nullptr, pl, err);
+  if (st != MUON_OK) { g_last_error = err; return st; }
+  *bytes = pl.total;
+  return MUON_OK;
+}
+
+muon_status muon_init(muon_ctx** out, const muon_config* cfg, const muon_tensor* params,
+                      const muon_tensor* grads, const int32_t* kinds, int32_t n, void* state_buf,
+                      size_t state_bytes, void* hip_stream) {
+  std::string err;
+  if (!out) { g_last_error = "out is NULL"; return MUON_E_ARG; }
+  *out = nullptr;
+  muon_status st = validate_list(cfg, params, grads, kinds, n, true, err);
+  if (st != MUON_OK) { g_last_error = err; return st; }
+  Plan probe;
+  st = build_plan(*cfg, params, kinds, n, nullptr, probe, err);
+  if (st != MUON_OK) { g_last_error = err; return st; }
+  if (probe.total > 0 && (!state_buf || reinterpret_cast<uintptr_t>(state_buf) % kAlign)) {
+    g_last_error = "state buffer is NULL or not 256-byte aligned";
+    return state_buf ? MUON_E_ALIGN : MUON_E_WORKSPACE;
+  }
+  if (state_bytes < probe.total) {
+    g_last_error = "state buffer too small: need " + std::to_string(probe.total) + " bytes";
+    return MUON_E_WORKSPACE;
+  }
+  muon_ctx* ctx = new (std::nothrow) muon_ctx();
+  if (!ctx) { g_last_error = "out of host memory"; return MUON_E_STATE; }
+  ctx->cfg = *cfg;
+  ctx->stream = static_cast<hipStream_t>(hip_stream);
+  ctx->base = static_cast<char*>(state_buf);
+  ctx->n = n;
+  ctx->params.assign(params, params + n);
+  ctx->grads.assign(grads, grads + n);
+  ctx->kinds.assign(kinds, kinds + n);
+  build_plan(*cfg, params, kinds, n, ctx->base, ctx->plan, err);
+  Plan& pl = ctx->plan;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t k = pl.table_index[i];
+    if (kinds[i] == MUON_KIND_MATRIX) {
+      pl.mats[k].w = static_cast<float*>(params[i].ptr);
+      pl.mats[k].g = grads[i].ptr;
+      pl.mats[k].gdt = grads[i].dtype;
+    } else {
+      pl.adams[k].p = static_cast<float*>(params[i].ptr);
+      pl.adams[k].g = grads[i].ptr;
+      pl.adams[k].gdt = grads[i].dtype;
+    }
+  }
+  auto fail = [&](hipError_t e, const char* what) {
+    char buf[256];
+    snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
+    g_last_error = buf;
+    delete ctx;
+    return MUON_E_HIP;
+  };
+  hipError_t e = hipGetDevice(&ctx->device);
+  if (e != hipSuccess) return fail(e, "hipGetDevice");
+  if (pl.zero_end) {
+    e = hipMemsetAsync(ctx->base, 0, pl.zero_end, ctx->stream);
+    if (e != hipSuccess) return fail(e, "hipMemsetAsync(state)");
+  }
+  const hipError_t ups[] = {
+      upload(ctx, pl.off_mats, pl.mats), upload(ctx, pl.off_adams, pl.adams),
+      upload(ctx, pl.off_col_tiles, pl.col_tiles), upload(ctx, pl.off_adam_chunks, pl.adam_chunks)};
+  for (hipError_t u : ups)
+    if (u != hipSuccess) return fail(u, "hipMemcpyAsync(tables)");
+  for (RowGroup& g : pl.row_groups) {
+    if ((e = upload(ctx, g.off_ids, g.ids)) != hipSuccess) return fail(e, "hipMemcpyAsync(rows)");
+    if ((e = upload(ctx, g.off_prefix, g.prefix)) != hipSuccess) return fail(e, "hipMemcpyAsync(rows)");
+  }
+  for (auto* plan : {&pl.ns_full, &pl.ns_block})
+    for (NsChunk& ch : *plan) {
+      if ((e = upload(ctx, ch.off_ns, ch.ns)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
+      if ((e = upload(ctx, ch.off_mom, ch.mom_items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
+      if ((e = upload(ctx, ch.off_cast, ch.cast_items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
+      for (auto& op : ch.gemm)
+        for (auto& gl : op)
+          if ((e = upload(ctx, gl.off, gl.items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
+    }
+  // The host copies of the tables must outlive the transfers.
+  if ((e = hipStreamSynchronize(ctx->stream)) != hipSuccess) return fail(e, "hipStreamSynchronize");
+  *out = ctx;
+  return MUON_OK;
+}
+
+muon_status muon_step(muon_ctx* ctx, const muon_tensor* params, const muon_tensor* grads,
+                      int64_t step) {
+  if (!ctx) return MUON_E_ARG;
+  if (ctx->broken) { ctx->err = "context unusable after an earlier HIP failure"; return MUON_E_STATE; }
+  if (step < 0) { ctx->err = "step must be >= 0"; return MUON_E_ARG; }
+  if (ctx->n > 0 && (!params || !grads)) { ctx->err = "params/grads is NULL"; return MUON_E_ARG; }
+  // validate everything before enqueueing anything
+  for (int32_t i = 0; i < ctx->n; ++i) {
+    const muon_tensor &p = params[i], &g = grads[i];
+    const muon_tensor &p0 = ctx->params[i], &g0 = ctx->grads[i];
+    std::string err;
+    muon_status st;
+    if ((st = check_ptr(p.ptr, "param", i, err)) != MUON_OK ||
+        (st = check_ptr(g.ptr, "grad", i, err)) != MUON_OK) {
+      ctx->err = err;
+      return st;
+    }
+    if (p.rows != p0.rows || p.cols != p0.cols || g.rows != g0.rows || g.cols != g0.cols) {
+      ctx->err = "tensor " + std::to_string(i) + ": shape differs from the init-time plan";
+      return MUON_E_SHAPE;
+    }
+    if (p.ld != p.cols || g.ld != g.cols) {
+      ctx->err = "tensor " + std::to_string(i) + ": ld must equal cols";
+      return MUON_E_ALIGN;
+    }
+    if (p.dtype != p0.dtype || g.dtype != g0.dtype) {
+      ctx->err = "tensor " + std::to_string(i) + ": dtype differs from the init-time plan";
+      return MUON_E_DTYPE;
+    }
+  }
+  Plan& pl = ctx->plan;
+  MatDev* mats = reinterpret_cast<MatDev*>(ctx->base + pl.off_mats);
+  AdamDev* adams = reinterpret_cast<AdamDev*>(ctx->base + pl.off_adams);
+  // patch moved pointers
+  PatchArgs pa[2]{};
+  pa[1].adam = 1;
+  for (int32_t i = 0; i < ctx->n; ++i) {
+    if (params[i].ptr == ctx->params[i].ptr && grads[i].ptr == ctx->grads[i].ptr) continue;
+    PatchArgs& a = pa[ctx->kinds[i] == MUON_KIND_ADAMW ? 1 : 0];
+    a.idx[a.count] = ctx->plan.table_index[i];
+    a.w[a.count] = params[i].ptr;
+    a.g[a.count] = grads[i].ptr;
+    ++a.count;
+    ctx->params[i].ptr = params[i].ptr;
+    ctx->grads[i].ptr = grads[i].ptr;
+    if (a.count == kPatchMax) {
+      const hipError_t e = launch_patch(ctx->stream, mats, adams, a);
+      if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "patch"); }
+      a.count = 0;
+    }
+  }
+  for (PatchArgs& a : pa) {
+    const hipError_t e = launch_patch(ctx->stream, mats, adams, a);
+    if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "patch"); }
+  }
+
+  const muon_config& c = ctx->cfg;
+  const int32_t br = muon_branch(&c, step);
+  muon_status st = MUON_OK;
+  if (!pl.mats.empty()) {
+    if (br == MUON_BRANCH_ROWNORM) {
+      StepScalars sc{c.lr, c.beta, c.gamma, c.eps_row, c.muon_wd};
+      for (RowGroup& g : pl.row_groups) {
+        const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_ROWS, launch_rownorm_rows(
+            ctx->stream, mats, reinterpret_cast<const int32_t*>(ctx->base + g.off_ids),
+            reinterpret_cast<const int64_t*>(ctx->base + g.off_prefix), int32_t(g.ids.size()),
+            g.prefix.back(), g.max_chunks, sc));
+        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_rows"); }
+      }
+      const TileItem* tiles = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_tiles);
+      for (int phase = 1; phase <= 2 && !pl.col_tiles.empty(); ++phase) {
+        const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_COLS1 + phase - 1,
+                                        launch_rownorm_cols(ctx->stream, mats, tiles,
+                                                            int64_t(pl.col_tiles.size()), phase, sc));
+        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_cols"); }
+      }
+    } else {
+      st = run_ns(ctx, br == MUON_BRANCH_NS5 ? pl.ns_full : pl.ns_block);
+      if (st != MUON_OK) { ctx->broken = true; return st; }
+    }
+  }
+  if (!pl.adams.empty()) {
+    const double n1 = double(step) + 1.0;
+    const float bc1 = float(1.0 - std::pow(double(c.adam_b1), n1));
+    const float bc2 = float(1.0 - std::pow(double(c.adam_b2), n1));
+    const hipError_t e = MUON_TIMED(ctx, MUON_K_ADAMW, launch_adamw(
+        ctx->stream, adams, reinterpret_cast<const AdamChunk*>(ctx->base + pl.off_adam_chunks),
+        int64_t(pl.adam_chunks.size()), c.adam_lr, c.adam_b1, c.adam_b2, c.adam_eps, c.adam_wd,
+        bc1, bc2));
+    if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "adamw"); }
+  }
+  return MUON_OK;
+}
+
+muon_status muon_state(const muon_ctx* ctx, int32_t i, int32_t which, muon_tensor* view) {
+  if (!ctx || !view) return MUON_E_ARG;
+  if (i < 0 || i >= ctx->n) return MUON_E_STATE;
+  const bool adam = ctx->kinds[i] == MUON_KIND_ADAMW;
+  if (which < 0 || which > (adam ? 1 : 0)) return MUON_E_ARG;
+  const Plan& pl = ctx->plan;
+  const size_t off = adam ? (which ? pl.v_off[i] : pl.m_off[i]) : pl.mom_off[i];
+  view->ptr = ctx->base + off;
+  view->rows = ctx->params[i].rows;
+  view->cols = ctx->params[i].cols;
+  view->ld = view->cols;
+  view->dtype = MUON_F32;
+  view->reserved = 0;
+  return MUON_OK;
+}
+
+int32_t muon_branch(const muon_config* cfg, int64_t step) {
+  if (!cfg || step < 0) return -1;
+  if (cfg->bp_blocks > 0) {
+    if (cfg->bp_period < 1) return -1;
+    return step % cfg->bp_period == 0 ? MUON_BRANCH_NS5 : MUON_BRANCH_BLOCK_NS5;
+  }
+  if (cfg->K < 1) return -1;
+  return step % cfg->K == 0 ? MUON_BRANCH_NS5 : MUON_BRANCH_ROWNORM;
+}
+
+muon_status muon_timing_enable(muon_ctx* ctx, int32_t enable) {
+  if (!ctx) return MUON_E_ARG;
+  ctx->timing = enable != 0;
+  return MUON_OK;
+}
+
+muon_status muon_timing_read(muon_ctx* ctx, double* ms, int64_t* launches) {
+  if (!ctx) return MUON_E_ARG;
+  double acc[MUON_K_COUNT] = {0};
+  int64_t cnt[MUON_K_COUNT] = {0};
+  for (size_t p = 0; p < ctx->events_used; ++p) {
+    hipError_t e = hipEventSynchronize(ctx->events[2 * p + 1]);
+    float dt = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&dt, ctx->events[2 * p], ctx->events[2 * p + 1]);
+    if (e != hipSuccess) {
+      ctx->events_used = 0;
+      return hip_fail(ctx, e, "muon_timing_read");
+    }
+    const int32_t k = ctx->event_class[p];
+    acc[k] += dt;
+    cnt[k] += 1;
+  }
+  ctx->events_used = 0;
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    if (ms) ms[k] = acc[k];
+    if (launches) launches[k] = cnt[k];
+  }
+  return MUON_OK;
+}
+
+void muon_free(muon_ctx* ctx) { delete ctx; }
+
+const char* muon_status_str(int32_t s) {
+  switch (s) {
+    case MUON_OK: return "ok";
+    case MUON_E_ARG: return "invalid argument";
+    case MUON_E_SHAPE: return "shape mismatch";
+    case MUON_E_DTYPE: return "dtype mismatch";
+    case MUON_E_ALIGN: return "misaligned or strided tensor";
+    case MUON_E_WORKSPACE: return "state buffer missing or too small";
+    case MUON_E_STATE: return "invalid context state";
+    case MUON_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* muon_last_error(const muon_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_last_error.c_str();
+}
+
+}  // extern "C"

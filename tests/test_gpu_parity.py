@@ -1,0 +1,405 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle.
+
+Protocol (per matrix, relative Frobenius error ||Y - Y*|| / ||Y*|| in fp64 on
+the host, absolute when ||Y*|| = 0):
+  * both sides run free from the same seeded inputs: the oracle keeps its own
+    fp64 momentum and never sees a value computed on the GPU;
+  * momentum M_t            <= 1e-5
+  * direction U_t, read as -W_t / lr from a weight that is zero before the
+    step:  RowNorm <= 1e-5, fp32-MFMA NS5 <= 1e-3, bf16-MFMA NS5 <= 2e-2;
+  * branch indexing bit-exact (muon_branch, and the observed U: long-axis
+    slice norms equal gamma exactly on RowNorm steps only).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_MOMENTUM = 1e-5
+TOL_ROWNORM = 1e-5
+TOL_NS5 = {0: 2e-2, 1: 1e-3}     # ns_precision: bf16, f32
+
+
+def _lib():
+    import matrix_aware_optimizer_periodic_amd as m
+    m.lib()                        # raises if the HIP library is missing
+    return m
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    d = np.linalg.norm(a - b)
+    return d / nb if nb > 0 else d
+
+
+def oracle_cfg(m, cfg):
+    return oracle.OracleConfig(
+        lr=float(np.float32(cfg.lr)), beta=float(np.float32(cfg.beta)),
+        gamma=float(np.float32(cfg.gamma)), eps_row=float(np.float32(cfg.eps_row)), K=cfg.K,
+        ns_iters=cfg.ns_iters, ns_a=float(np.float32(cfg.ns_a)),
+        ns_b=float(np.float32(cfg.ns_b)), ns_c=float(np.float32(cfg.ns_c)),
+        ns_eps=float(np.float32(cfg.ns_eps)), rownorm_axis=cfg.rownorm_axis,
+        bp_blocks=cfg.bp_blocks, bp_period=cfg.bp_period,
+        bp_lr_ratio=float(np.float32(cfg.bp_lr_ratio)), muon_wd=float(np.float32(cfg.muon_wd)),
+        adam_lr=float(np.float32(cfg.adam_lr)), adam_b1=float(np.float32(cfg.adam_b1)),
+        adam_b2=float(np.float32(cfg.adam_b2)), adam_eps=float(np.float32(cfg.adam_eps)),
+        adam_wd=float(np.float32(cfg.adam_wd)))
+
+
+def dir_tol(br, prec):
+    return TOL_ROWNORM if br == oracle.BRANCH_ROWNORM else TOL_NS5[prec]
+
+
+def run_direction_parity(shapes, steps, grad_dtype="bf16", grad_std=1e-3, seed=0,
+                         shape_grads=None, **over):
+    """Run `steps` steps with W zeroed before each; check M_t and U_t."""
+    m = _lib()
+    tdt = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    G = [torch.zeros(s, dtype=tdt, device="cuda") for s in shapes]
+    sess = m.MuonSession(W, G, kinds=[m.MUON_KIND_MATRIX] * len(shapes), **over)
+    try:
+        return _direction_loop(sess, shapes, steps, W, G, tdt, grad_dtype, grad_std, seed,
+                               shape_grads)
+    finally:
+        sess.close()
+
+
+def _direction_loop(sess, shapes, steps, W, G, tdt, grad_dtype, grad_std, seed, shape_grads):
+    m = _lib()
+    ocfg = oracle_cfg(m, sess.cfg)
+    Mo = [np.zeros(s) for s in shapes]
+    worst = {}
+    for t in range(steps):
+        gh = []
+        for i, s in enumerate(shapes):
+            g = workloads.host_grad(seed, t, i, s, grad_std, grad_dtype)
+            if shape_grads is not None:
+                g = shape_grads(i, t, g)
+            gh.append(g)
+            G[i].copy_(torch.from_numpy(g).to(tdt))
+            W[i].zero_()
+        sess.step(t)
+        torch.cuda.synchronize()
+        br = sess.branch(t)
+        assert br == oracle.branch(t, ocfg)
+        for i, s in enumerate(shapes):
+            Mo[i] = oracle.momentum_update(Mo[i], gh[i], ocfg.beta)
+            Uo, lr = oracle.direction(Mo[i], t, ocfg)
+            Ug = -W[i].double().cpu().numpy() / lr
+            Mg = sess.state_view(i).double().cpu().numpy()
+            em = rel(Mg, Mo[i])
+            eu = rel(Ug, Uo)
+            tol = dir_tol(br, sess.cfg.ns_precision)
+            worst[(br, s)] = max(worst.get((br, s), 0.0), eu)
+            print(f"t={t} shape={s} branch={br} momentum {em:.2e} direction {eu:.2e} "
+                  f"(tol {tol:g})", flush=True)
+            assert em <= TOL_MOMENTUM, f"t={t} shape={s} momentum err {em:.3e}"
+            assert eu <= tol, f"t={t} shape={s} branch={br} direction err {eu:.3e} > {tol}"
+            if br == oracle.BRANCH_ROWNORM:
+                axis = 0 if (s[0] > s[1] and sess.cfg.rownorm_axis == 0) else 1
+                norms = np.linalg.norm(Ug, axis=axis)
+                live = np.linalg.norm(Mo[i], axis=axis) > ocfg.eps_row
+                np.testing.assert_allclose(norms[live], ocfg.gamma, rtol=1e-5)
+    return worst
+
+
+# ------------------------------------------------------------------ single matrix
+@pytest.mark.parametrize("prec", [0, 1])
+def test_single_256x512_fp32_grads(prec):
+    """256 x 512 fp32 weight, N(0,1) fp32 grads, 6 steps: 2 refreshes, 4 RowNorm."""
+    wl = workloads.WORKLOADS["single-256x512"]
+    shapes = [(m_, n_) for _, m_, n_ in wl.shapes]
+    worst = run_direction_parity(shapes, wl.steps, grad_dtype="f32", grad_std=wl.grad_std,
+                                 ns_precision=prec)
+    print({k: f"{v:.2e}" for k, v in worst.items()})
+
+
+def test_single_256x512_ns5_against_svd_polar_band():
+    """The refresh direction shares its singular vectors with the SVD polar
+    factor and its singular values follow the quintic's band."""
+    m = _lib()
+    W = torch.zeros(256, 512, device="cuda")
+    g = workloads.host_grad(0, 0, 0, (256, 512), 1.0, "f32")
+    G = torch.from_numpy(g).cuda()
+    sess = m.MuonSession([W], [G], ns_precision=1)
+    sess.step(0)
+    torch.cuda.synchronize()
+    U = -W.double().cpu().numpy() / np.float32(sess.cfg.lr)
+    u, s, vt = np.linalg.svd(g.astype(np.float64), full_matrices=False)
+    D = u.T @ U @ vt.T
+    off = D - np.diag(np.diag(D))
+    assert np.linalg.norm(off) / np.linalg.norm(D) < 1e-3
+    x = s / (np.linalg.norm(g) + 1e-7)
+    assert np.all((np.diag(D)[x > 5.2e-3] > 0.68) & (np.diag(D)[x > 5.2e-3] < 1.14))
+    sess.close()
+
+
+# ------------------------------------------------------------------ ragged sets
+RAGGED = [(300, 700), (700, 300), (128, 128), (1, 64), (64, 1), (260, 260), (33, 2050),
+          (2050, 33), (1200, 1030)]
+
+
+@pytest.mark.parametrize("prec", [0, 1])
+def test_ragged_mixed_set(prec):
+    """Tall, wide, square, single-row/column and non-tile-multiple shapes in
+    one grouped launch set, bf16 grads, several tiles and ragged tails."""
+    run_direction_parity(RAGGED, 6, ns_precision=prec)
+
+
+def test_edge_values_zero_and_subthreshold_slices():
+    """A zero gradient matrix, zero rows, and rows whose norm stays below eps."""
+    shapes = [(64, 256), (256, 64), (40, 96)]
+
+    def edit(i, t, g):
+        g = g.copy()
+        if i == 2:
+            g[:] = 0.0
+        else:
+            if shapes[i][0] <= shapes[i][1]:
+                g[3] = 0.0
+                g[7] = workloads.round_to_bf16(g[7] * np.float32(1e-9))
+            else:
+                g[:, 3] = 0.0
+                g[:, 7] = workloads.round_to_bf16(g[:, 7] * np.float32(1e-9))
+        return g
+    run_direction_parity(shapes, 6, shape_grads=edit, ns_precision=1)
+
+
+def test_rownorm_stored_rows_mode():
+    run_direction_parity([(512, 96), (96, 512), (257, 31)], 3, rownorm_axis=1)
+
+
+def test_vanilla_muon_K1():
+    run_direction_parity([(256, 640), (640, 256)], 3, K=1, ns_precision=1)
+
+
+def test_muonbp_blocks():
+    """MuonBP: full NS5 every 3rd step, 8 column blocks orthogonalised on
+    their own with half the step size otherwise."""
+    run_direction_parity([(512, 1024), (1024, 512), (384, 384)], 6, bp_blocks=8, bp_period=3,
+                         ns_precision=1)
+    run_direction_parity([(512, 1024), (1024, 512)], 3, bp_blocks=8, bp_period=3,
+                         ns_precision=0)
+
+
+def test_long_rows_streaming_path():
+    """Rows longer than the register-resident limit take the two-pass path."""
+    run_direction_parity([(4, 40000), (3, 33001)], 3)
+
+
+# ------------------------------------------------------------------ whole step
+def test_weight_accumulation_and_decay_free_running():
+    m = _lib()
+    shapes = [(200, 520), (520, 200)]
+    W0 = [workloads.host_weight0(0, i, s) for i, s in enumerate(shapes)]
+    W = [torch.from_numpy(w).cuda() for w in W0]
+    G = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    sess = m.MuonSession(W, G, muon_wd=0.01, ns_precision=1)
+    ocfg = oracle_cfg(m, sess.cfg)
+    Wo = [w.astype(np.float64) for w in W0]
+    Mo = [np.zeros(s) for s in shapes]
+    for t in range(6):
+        for i, s in enumerate(shapes):
+            g = workloads.host_grad(3, t, i, s, 1e-3, "bf16")
+            G[i].copy_(torch.from_numpy(g).to(torch.bfloat16))
+            Wo[i], Mo[i], _ = oracle.muon_matrix_step(Wo[i], Mo[i], g, t, ocfg)
+        sess.step(t)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        Wg = W[i].double().cpu().numpy()
+        assert rel(Wg - W0[i], Wo[i] - W0[i]) <= 1e-3
+        assert rel(Wg, Wo[i]) <= 1e-5
+    sess.close()
+
+
+def test_adamw_tensors():
+    m = _lib()
+    sizes = [(1, 3), (1, 4096), (1, 5000), (1, 12289)]
+    P0 = [workloads.host_weight0(1, i, s) for i, s in enumerate(sizes)]
+    P = [torch.from_numpy(p).cuda().view(-1) for p in P0]
+    G = [torch.zeros(s[1], dtype=torch.bfloat16 if i % 2 else torch.float32, device="cuda")
+         for i, s in enumerate(sizes)]
+    sess = m.MuonSession(P, G, adam_wd=0.01, adam_lr=3e-3)
+    ocfg = oracle_cfg(m, sess.cfg)
+    st = [(np.zeros(s[1]), np.zeros(s[1])) for s in sizes]
+    po = [p.astype(np.float64).reshape(-1) for p in P0]
+    for t in range(5):
+        for i, s in enumerate(sizes):
+            dt = "bf16" if i % 2 else "f32"
+            g = workloads.host_grad(5, t, i, (s[1],), 1e-2, dt)
+            G[i].copy_(torch.from_numpy(g).to(G[i].dtype))
+            po[i], mo, vo = oracle.adamw_step(po[i], g, st[i][0], st[i][1], t, ocfg)
+            st[i] = (mo, vo)
+        sess.step(t)
+    torch.cuda.synchronize()
+    for i in range(len(sizes)):
+        pg = P[i].double().cpu().numpy()
+        assert rel(pg - P0[i].reshape(-1), po[i] - P0[i].reshape(-1)) <= 1e-5
+        assert rel(sess.state_view(i, 0).double().cpu().numpy().reshape(-1), st[i][0]) <= 1e-5
+        assert rel(sess.state_view(i, 1).double().cpu().numpy().reshape(-1), st[i][1]) <= 1e-5
+    sess.close()
+
+
+def _run_steps(m, shapes, steps, t0=0, state=None, **over):
+    W = [torch.from_numpy(workloads.host_weight0(7, i, s)).cuda() for i, s in enumerate(shapes)]
+    G = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    sess = m.MuonSession(W, G, **over)
+    if state is not None:
+        for i in range(len(shapes)):
+            sess.state_view(i).copy_(state[1][i])
+            W[i].copy_(state[0][i])
+    for t in range(t0, t0 + steps):
+        for i, s in enumerate(shapes):
+            G[i].copy_(torch.from_numpy(workloads.host_grad(8, t, i, s, 1e-3, "bf16")).to(torch.bfloat16))
+        sess.step(t)
+    torch.cuda.synchronize()
+    out = ([w.clone() for w in W], [sess.state_view(i).clone() for i in range(len(shapes))])
+    sess.close()
+    return out
+
+
+def test_determinism_and_resume_bitwise():
+    """Two runs are bitwise identical (no unordered reductions); 3 steps,
+    checkpoint through muon_state views, fresh context, 3 more steps equals 6
+    straight steps bitwise."""
+    m = _lib()
+    shapes = [(512, 1536), (1536, 512), (300, 700)]
+    a = _run_steps(m, shapes, 6)
+    b = _run_steps(m, shapes, 6)
+    for x, y in zip(a[0] + a[1], b[0] + b[1]):
+        assert torch.equal(x, y)
+    half = _run_steps(m, shapes, 3)
+    ckpt = ([w.cpu() for w in half[0]], [s.cpu() for s in half[1]])
+    resumed = _run_steps(m, shapes, 3, t0=3, state=ckpt)
+    for x, y in zip(a[0] + a[1], resumed[0] + resumed[1]):
+        assert torch.equal(x, y)
+
+
+def test_pointer_change_between_steps():
+    """Passing other W / G buffers on a step patches the launch tables."""
+    m = _lib()
+    shapes = [(256, 512), (512, 256)]
+    W1 = [torch.zeros(s, device="cuda") for s in shapes]
+    G1 = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    sess = m.MuonSession(W1, G1, ns_precision=1)
+    W2 = [torch.zeros(s, device="cuda") for s in shapes]
+    G2 = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    ocfg = oracle_cfg(m, sess.cfg)
+    Mo = [np.zeros(s) for s in shapes]
+    for t in range(4):
+        Wt, Gt = (W1, G1) if t % 2 == 0 else (W2, G2)
+        for i, s in enumerate(shapes):
+            g = workloads.host_grad(9, t, i, s, 1e-3, "bf16")
+            Gt[i].copy_(torch.from_numpy(g).to(torch.bfloat16))
+            Wt[i].zero_()
+            Mo[i] = oracle.momentum_update(Mo[i], g, ocfg.beta)
+        sess.step(t, params=Wt, grads=Gt)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            Uo, lr = oracle.direction(Mo[i], t, ocfg)
+            assert rel(-Wt[i].double().cpu().numpy() / lr, Uo) <= dir_tol(sess.branch(t), 1)
+    sess.close()
+
+
+def test_step_validation_on_device_context():
+    m = _lib()
+    W = [torch.zeros(64, 128, device="cuda")]
+    G = [torch.zeros(64, 128, dtype=torch.bfloat16, device="cuda")]
+    sess = m.MuonSession(W, G)
+    with pytest.raises(m.MuonError) as e:
+        sess.step(-1)
+    assert e.value.status == m.binding.MUON_E_ARG
+    with pytest.raises(m.MuonError) as e:
+        sess.step(0, grads=[torch.zeros(64, 128, device="cuda")])
+    assert e.value.status == m.binding.MUON_E_DTYPE
+    bad = m.tensor_desc(torch.zeros(64, 130, device="cuda"))
+    with pytest.raises(m.MuonError) as e:
+        m.muon_step(sess.ctx, [bad], sess.gdesc, 0)
+    assert e.value.status == m.binding.MUON_E_SHAPE
+    sess.close()
+
+
+def test_empty_parameter_list():
+    m = _lib()
+    cfg = m.muon_config_default()
+    assert m.muon_state_bytes(cfg, [], []) == 0
+    ctx = m.muon_init(cfg, [], [], [], 0, 0, 0)
+    m.muon_step(ctx, [], [], 0)
+    m.muon_free(ctx)
+
+
+# ------------------------------------------------------------------ full size
+def _dit_full_set(m, wl, seed=0):
+    dev = torch.device("cuda")
+    shapes = [(a, b) for _, a, b in wl.shapes]
+    params = [workloads.device_normal_(torch.empty(s, device=dev), 0.02, workloads.seed_for(seed, 0, i, 2))
+              for i, s in enumerate(shapes)]
+    grads = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
+    kinds = [m.MUON_KIND_MATRIX] * len(shapes)
+    for b in range(wl.blocks):
+        for j, L in enumerate(workloads.dit_bias_sizes(wl.d)):
+            params.append(torch.zeros(L, device=dev))
+            grads.append(torch.zeros(L, dtype=torch.bfloat16, device=dev))
+            kinds.append(m.MUON_KIND_ADAMW)
+    return shapes, params, grads, kinds
+
+
+@pytest.mark.parametrize("name", ["dit-1.3b"])
+def test_dit_full_set_sampled(name):
+    """The whole DiT-shaped set in one context, as the benchmark runs it.
+    One matrix of each shape (from different blocks) is compared with the
+    oracle at every step; on the RowNorm step every matrix is checked for
+    long-axis slice norms of gamma (a property that holds at any size)."""
+    m = _lib()
+    wl = workloads.WORKLOADS[name]
+    shapes, params, grads, kinds = _dit_full_set(m, wl)
+    per = len(workloads.dit_block_shapes(wl.d))
+    sample = [b * per + k for b, k in [(3, 0), (wl.blocks - 1, 1), (9, 2), (0, 3), (11, 4)]]
+    probes = {i: torch.zeros(shapes[i], device="cuda") for i in sample}
+    sess = m.MuonSession(params, grads, kinds=kinds)
+    try:
+        ocfg = oracle_cfg(m, sess.cfg)
+        Mo = {i: np.zeros(shapes[i]) for i in sample}
+        for t in range(3):
+            for i, s in enumerate(shapes):
+                workloads.device_normal_(grads[i], wl.grad_std, workloads.seed_for(0, t, i, 1))
+            for p in probes.values():
+                p.zero_()
+            step_params = [probes.get(i, p) for i, p in enumerate(params)]
+            before = [p.clone() for p in params[:len(shapes)]] if t == 1 else None
+            sess.step(t, params=step_params)
+            torch.cuda.synchronize()
+            br = sess.branch(t)
+            assert br == oracle.branch(t, ocfg)
+            for i in sample:
+                g = grads[i].float().cpu().double().numpy()
+                Mo[i] = oracle.momentum_update(Mo[i], g, ocfg.beta)
+                Uo, lr = oracle.direction(Mo[i], t, ocfg)
+                Ug = -probes[i].double().cpu().numpy() / lr
+                em = rel(sess.state_view(i).double().cpu().numpy(), Mo[i])
+                eu = rel(Ug, Uo)
+                print(f"{name} t={t} matrix {i} {shapes[i]} branch {br}: momentum {em:.2e} "
+                      f"direction {eu:.2e}", flush=True)
+                assert em <= TOL_MOMENTUM
+                assert eu <= dir_tol(br, sess.cfg.ns_precision)
+            if before is not None:
+                worst = 0.0
+                for i, s in enumerate(shapes):
+                    if i in probes:
+                        continue
+                    dU = (before[i] - params[i]).double() / ocfg.lr
+                    norms = dU.norm(dim=0 if s[0] > s[1] else 1)
+                    worst = max(worst, float(((norms - ocfg.gamma).abs() / ocfg.gamma).max()))
+                print(f"{name} RowNorm step: worst slice-norm deviation {worst:.2e}", flush=True)
+                assert worst <= 2e-3
+                del before
+    finally:
+        sess.close()
