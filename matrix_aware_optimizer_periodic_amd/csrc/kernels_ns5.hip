@@ -36,6 +36,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
+// Pointers into global memory.  The workspace pointers come out of launch
+// tables, so the compiler cannot tell they are global; without the address
+// space it emits flat loads, which also count against the LDS wait counter
+// and would make every LDS fragment wait also wait for in-flight global loads.
+#define GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ GLOBAL T* as_global(T* p) {
+  return (GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ const GLOBAL T* as_global(const T* p) {
+  return (const GLOBAL T*)(p);
+}
+
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -183,15 +197,15 @@ __global__ __launch_bounds__(kThreads) void ns_cast_kernel(
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float v[8]) {
   if constexpr (sizeof(T) == 2) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t u = *as_global(reinterpret_cast<const u32x4_t*>(p));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       v[2 * k] = bf16_to_f32(u[k] & 0xffffu);
       v[2 * k + 1] = bf16_to_f32(u[k] >> 16);
     }
   } else {
-    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
-    const f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+    const f32x4_t a = as_global(reinterpret_cast<const f32x4_t*>(p))[0];
+    const f32x4_t b = as_global(reinterpret_cast<const f32x4_t*>(p))[1];
 #pragma unroll
     for (int k = 0; k < 4; ++k) { v[k] = a[k]; v[4 + k] = b[k]; }
   }
@@ -203,10 +217,10 @@ __device__ __forceinline__ void store8(T* p, const float v[8]) {
     u32x4_t u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) u[k] = f32_to_bf16(v[2 * k]) | (f32_to_bf16(v[2 * k + 1]) << 16);
-    *reinterpret_cast<u32x4_t*>(p) = u;
+    *as_global(reinterpret_cast<u32x4_t*>(p)) = u;
   } else {
-    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
-    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+    as_global(reinterpret_cast<f32x4_t*>(p))[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+    as_global(reinterpret_cast<f32x4_t*>(p))[1] = f32x4_t{v[4], v[5], v[6], v[7]};
   }
 }
 
@@ -214,27 +228,33 @@ __device__ __forceinline__ void store8(T* p, const float v[8]) {
 // last Newton-Schulz round), vectorised when the run is whole and aligned.
 __device__ __forceinline__ void w_update8(float* w, int64_t e0, int nv, const float v[8], float lr,
                                           float keep) {
+  GLOBAL float* gw = as_global(w) + e0;
   if (nv == 8 && (e0 & 3) == 0) {
-    f32x4_t a = reinterpret_cast<f32x4_t*>(w + e0)[0];
-    f32x4_t b = reinterpret_cast<f32x4_t*>(w + e0)[1];
+    f32x4_t a = reinterpret_cast<GLOBAL f32x4_t*>(gw)[0];
+    f32x4_t b = reinterpret_cast<GLOBAL f32x4_t*>(gw)[1];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       a[k] = fmaf(-lr, v[k], a[k] * keep);
       b[k] = fmaf(-lr, v[4 + k], b[k] * keep);
     }
-    reinterpret_cast<f32x4_t*>(w + e0)[0] = a;
-    reinterpret_cast<f32x4_t*>(w + e0)[1] = b;
+    reinterpret_cast<GLOBAL f32x4_t*>(gw)[0] = a;
+    reinterpret_cast<GLOBAL f32x4_t*>(gw)[1] = b;
   } else {
-    for (int u = 0; u < nv; ++u) w[e0 + u] = fmaf(-lr, v[u], w[e0 + u] * keep);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < nv) gw[u] = fmaf(-lr, v[u], gw[u] * keep);
   }
 }
 
 // GEMM tile C[i0.., j0..] = sum_k P[i][k] Q[j][k] on MFMA, BM x BM per
-// workgroup of 4 waves (2 x 2), each wave (BM/2) x (BM/2) built from 32 x 32
-// MFMA blocks.  The k loop stages 128-byte rows (64 bf16 or 32 fp32) of P and
-// Q through LDS, double-buffered, with the 16-byte chunks of each row XOR-
-// swizzled by (row & 7) so the fragment reads of 32 consecutive rows hit
-// distinct banks.
+// workgroup of WGM x WGN waves, each wave (BM/WGM) x (BM/WGN) built from
+// 32 x 32 MFMA blocks.  256-tiles run 8 waves (two per SIMD, so one wave's
+// MFMAs cover the other's memory waits); 128-tiles run 4.  The k loop stages
+// 128-byte rows (64 bf16 or 32 fp32) of P and Q through LDS, double-
+// buffered.  The 16-byte chunks of LDS row r are XOR-swizzled by
+// ((r >> 1) & 7): gfx950 serves a 128-bit LDS read in groups of 16 lanes over
+// 64 banks, and with this swizzle the 16 consecutive rows that such a group
+// reads at one logical chunk land on 16 distinct bank groups.
 //
 // MFMA operand layout used (both 32 x 32 variants): lane l supplies row
 // (l & 31) of P and of Q; its k values are the 16-byte chunk 2g + (l >> 5) of
@@ -254,20 +274,25 @@ __device__ __forceinline__ void w_update8(float* w, int64_t e0, int nv, const fl
 // A_ii.  This is the same arithmetic, rounded later: it avoids the
 // cancellation between a and B_ii that bf16 storage of B_ii would amplify
 // when the short side r is small.
-template <typename T, int BM, int OP>
-__global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
+template <typename T, int BM, int WGM, int WGN, int OP>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
     const GemmItem* __restrict__ items, int iter, int last, float ca, float cb, float cc,
     float wd) {
-  constexpr int WM = BM / 2;
-  constexpr int FM = WM / 32;
+  constexpr int NT = 64 * WGM * WGN;         // threads
+  constexpr int WM = BM / WGM, WN = BM / WGN;
+  constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int ROWS = 2 * BM;               // P rows then Q rows
-  constexpr int LOADS = ROWS * 8 / kThreads; // 16-byte loads per thread per stage
+  constexpr int RPL = NT / 8;                // LDS rows covered by one load round
+  constexpr int LOADS = ROWS / RPL;          // 16-byte loads per thread per stage
   constexpr int KT = 128 / int(sizeof(T));   // k elements per stage
   constexpr int SLD = BM + 4;                // epilogue stage row stride (floats)
+  constexpr int HALF = BM / 2;
   constexpr int MAIN_BYTES = 2 * ROWS * 128;
-  constexpr int STAGE_BYTES = WM * SLD * 4;
+  constexpr int STAGE_BYTES = HALF * SLD * 4;
   constexpr int SMEM = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
+  static_assert(WM <= HALF && HALF % WM == 0, "a wave's rows must sit in one half");
+  static_assert(BM % RPL == 0, "load rounds must not straddle P and Q");
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   u32x4_t* lds = reinterpret_cast<u32x4_t*>(smem);
 
@@ -282,18 +307,21 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
   } else if constexpr (OP == kGemmPoly) {
     P = Q = static_cast<const T*>(d.a); ld = d.rp; K = d.rp;
   } else {
-    P = static_cast<const T*>(d.b); Q = static_cast<const T*>(d.xc[cur]); ld = d.rp; K = d.rp;
+    P = static_cast<const T*>(d.b);
+    Q = static_cast<const T*>(cur ? d.xc[1] : d.xc[0]);
+    ld = d.rp;
+    K = d.rp;
   }
   const int64_t i0 = int64_t(it.ti) * BM, j0 = int64_t(it.tj) * BM;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WGN, wn = wid % WGN;
 
-  // Global -> LDS mapping: load L covers LDS rows 32 L .. 32 L + 31.
+  // Global -> LDS mapping: load round L covers LDS rows RPL L .. RPL L + RPL-1.
   const int lrow = tid >> 3, lch = tid & 7;
   const char* gP = reinterpret_cast<const char*>(P + (i0 + lrow) * ld) + lch * 16;
   const char* gQ = reinterpret_cast<const char*>(Q + (j0 + lrow) * ld) + lch * 16;
-  const int64_t gstride = 32 * ld * int64_t(sizeof(T));
-  const int sofs = lrow * 8 + (lch ^ (lrow & 7));
+  const int64_t gstride = int64_t(RPL) * ld * int64_t(sizeof(T));
+  const int sofs = lrow * 8 + (lch ^ ((lrow >> 1) & 7));
 
   u32x4_t stg[LOADS];
   auto gload = [&](int kt) {
@@ -301,55 +329,77 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
 #pragma unroll
     for (int L = 0; L < LOADS; ++L) {
       const char* src = (L < LOADS / 2) ? gP + L * gstride : gQ + (L - LOADS / 2) * gstride;
-      stg[L] = *reinterpret_cast<const u32x4_t*>(src + kb);
+      stg[L] = *as_global(reinterpret_cast<const u32x4_t*>(src + kb));
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int L = 0; L < LOADS; ++L) lds[buf * ROWS * 8 + L * 256 + sofs] = stg[L];
+    for (int L = 0; L < LOADS; ++L) lds[buf * ROWS * 8 + L * RPL * 8 + sofs] = stg[L];
   };
 
-  f32x16_t acc[FM][FM];
+  f32x16_t acc[FM][FN];
 #pragma unroll
   for (int a = 0; a < FM; ++a)
 #pragma unroll
-    for (int b = 0; b < FM; ++b) acc[a][b] = (f32x16_t)(0.0f);
+    for (int b = 0; b < FN; ++b) acc[a][b] = (f32x16_t)(0.0f);
 
   const int nk = int(K / KT);
   gload(0);
   sstore(0);
   __syncthreads();
-  const int frow = lane & 31, fsw = lane & 7, fhalf = lane >> 5;
+  const int frow = lane & 31, fsw = (lane >> 1) & 7, fhalf = lane >> 5;
+  // Fragments of k-group g (16 k values) for this wave's FM x FN MFMA blocks.
+  auto frag = [&](const u32x4_t* sP, const u32x4_t* sQ, int g, u32x4_t* fa, u32x4_t* fb) {
+    const int ch = (2 * g + fhalf) ^ fsw;
+#pragma unroll
+    for (int f = 0; f < FM; ++f) fa[f] = sP[(wm * WM + f * 32 + frow) * 8 + ch];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) fb[f] = sQ[(wn * WN + f * 32 + frow) * 8 + ch];
+  };
+  auto mma = [&](const u32x4_t* fa, const u32x4_t* fb) {
+#pragma unroll
+    for (int x = 0; x < FM; ++x)
+#pragma unroll
+      for (int y = 0; y < FN; ++y) {
+        if constexpr (sizeof(T) == 2) {
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, fa[x]), __builtin_bit_cast(bf16x8_t, fb[y]), acc[x][y],
+              0, 0, 0);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                __uint_as_float(fa[x][s]), __uint_as_float(fb[y][s]), acc[x][y], 0, 0, 0);
+        }
+      }
+  };
+  // Main loop: the global loads of stage kt+1 are in flight during the
+  // MFMAs of stage kt; within a stage the LDS fragments of k-group g+1 are
+  // read while the MFMAs of group g run (two fragment register sets).  The
+  // sched_barrier(0) fences keep the compiler from sinking each fragment
+  // read next to its first use, which would expose every LDS latency.
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
     const u32x4_t* sP = lds + buf * ROWS * 8;
     const u32x4_t* sQ = sP + BM * 8;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int ch = (2 * g + fhalf) ^ fsw;
-      u32x4_t af[FM], bfr[FM];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        af[f] = sP[(wm * WM + f * 32 + frow) * 8 + ch];
-        bfr[f] = sQ[(wn * WM + f * 32 + frow) * 8 + ch];
-      }
-#pragma unroll
-      for (int fa = 0; fa < FM; ++fa)
-#pragma unroll
-        for (int fb = 0; fb < FM; ++fb) {
-          if constexpr (sizeof(T) == 2) {
-            acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, af[fa]), __builtin_bit_cast(bf16x8_t, bfr[fb]),
-                acc[fa][fb], 0, 0, 0);
-          } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                  __uint_as_float(af[fa][s]), __uint_as_float(bfr[fb][s]), acc[fa][fb], 0, 0, 0);
-          }
-        }
-    }
+    u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
+    frag(sP, sQ, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    frag(sP, sQ, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    frag(sP, sQ, 2, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    frag(sP, sQ, 3, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
   }
@@ -358,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
   float* stage = reinterpret_cast<float*>(smem);
   const bool diag_tile = it.ti == it.tj;
   T* xr = static_cast<T*>(d.xr);
-  T* xcn = static_cast<T*>(d.xc[cur ^ 1]);
+  T* xcn = static_cast<T*>(cur ? d.xc[0] : d.xc[1]);
   float* w = mats[d.mat].w;
   const float wkeep = 1.0f - d.lr * wd;
   bool mirror;
@@ -367,21 +417,22 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
 
 #pragma unroll 1
   for (int half = 0; half < 2; ++half) {
-    if (wm == half) {
+    if ((wm * WM) / HALF == half) {
+      const int rbase = wm * WM - half * HALF;
 #pragma unroll
       for (int fa = 0; fa < FM; ++fa)
 #pragma unroll
-        for (int fb = 0; fb < FM; ++fb)
+        for (int fb = 0; fb < FN; ++fb)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            stage[(fa * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3)) * SLD + wn * WM + fb * 32 + frow] =
-                acc[fa][fb][v];
+            stage[(rbase + fa * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3)) * SLD + wn * WN + fb * 32 +
+                  frow] = acc[fa][fb][v];
     }
     __syncthreads();
-    const int64_t ib0 = i0 + int64_t(half) * WM;
+    const int64_t ib0 = i0 + int64_t(half) * HALF;
     // rows of the tile: C[i][j .. j+7]
     constexpr int CPR = BM / 8;
-    for (int idx = tid; idx < WM * CPR; idx += kThreads) {
+    for (int idx = tid; idx < HALF * CPR; idx += NT) {
       const int r = idx / CPR, ch = idx % CPR;
       const int64_t i = ib0 + r, j = j0 + ch * 8;
       float* sv = stage + r * SLD + ch * 8;
@@ -389,25 +440,33 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = sv[u];
       const bool has_diag = diag_tile && i >= j && i < j + 8;
+      const int du = int(i - j);
       if constexpr (OP == kGemmGram) {
-        if (has_diag) d.adiag[i] = v[i - j];
+        if (has_diag) {
+          float dv = 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) dv = (u == du) ? v[u] : dv;
+          d.adiag[i] = dv;
+        }
         store8(static_cast<T*>(d.a) + i * d.rp + j, v);
       } else if constexpr (OP == kGemmPoly) {
         float av[8];
         load8(static_cast<const T*>(d.a) + i * d.rp + j, av);
         float dval = 0.f;
         if (has_diag) {
-          const int u = int(i - j);
-          const float ad = d.adiag[i];
-          const float aa = v[u] + ad * ad - av[u] * av[u];
-          dval = fmaf(cb, ad, cc * aa);
-        }
+          float acc_ii = 0.f, a_ii = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = fmaf(cc, v[u], cb * av[u]);
-        if (has_diag) {
-          v[i - j] = 0.f;
+          for (int u = 0; u < 8; ++u) {
+            acc_ii = (u == du) ? v[u] : acc_ii;
+            a_ii = (u == du) ? av[u] : a_ii;
+          }
+          const float ad = d.adiag[i];
+          const float aa = acc_ii + ad * ad - a_ii * a_ii;
+          dval = fmaf(cb, ad, cc * aa);
           d.bdiag[i] = dval;
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (has_diag && u == du) ? 0.f : fmaf(cc, v[u], cb * av[u]);
         store8(static_cast<T*>(d.b) + i * d.rp + j, v);
 #pragma unroll
         for (int u = 0; u < 8; ++u) sv[u] = v[u];
@@ -435,8 +494,8 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
     __syncthreads();
     // columns of the tile: C[i .. i+7][j] written as row j of the transpose
     if (mirror) {
-      constexpr int CPC = WM / 8;
-      for (int idx = tid; idx < BM * CPC; idx += kThreads) {
+      constexpr int CPC = HALF / 8;
+      for (int idx = tid; idx < BM * CPC; idx += NT) {
         const int jj = idx / CPC, ch = idx % CPC;
         const int64_t j = j0 + jj, i = ib0 + ch * 8;
         float v[8];
@@ -460,20 +519,26 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(
   }
 }
 
+// 256-tiles: 8 waves in a 2 x 4 grid; 128-tiles: 4 waves in 2 x 2.
+template <int BM> struct WaveGrid;
+template <> struct WaveGrid<256> { static constexpr int M = 2, N = 4; };
+template <> struct WaveGrid<128> { static constexpr int M = 2, N = 2; };
+
 template <typename T, int BM>
 hipError_t launch_gemm_t(hipStream_t s, const MatDev* mats, const NsDev* ns,
                          const GemmItem* items, int64_t nitems, int op, int iter, int last,
                          float a, float b, float c, float wd) {
-  const dim3 grid(static_cast<unsigned>(nitems)), block(kThreads);
+  constexpr int GM = WaveGrid<BM>::M, GN = WaveGrid<BM>::N;
+  const dim3 grid(static_cast<unsigned>(nitems)), block(64 * GM * GN);
   switch (op) {
     case kGemmGram:
-      ns_gemm_kernel<T, BM, kGemmGram><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      ns_gemm_kernel<T, BM, GM, GN, kGemmGram><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
       break;
     case kGemmPoly:
-      ns_gemm_kernel<T, BM, kGemmPoly><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      ns_gemm_kernel<T, BM, GM, GN, kGemmPoly><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
       break;
     default:
-      ns_gemm_kernel<T, BM, kGemmProduct><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      ns_gemm_kernel<T, BM, GM, GN, kGemmProduct><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
       break;
   }
   return hipGetLastError();

@@ -187,6 +187,8 @@ size_t problem_ws_bytes(const Problem& p, int tile, size_t es, int64_t* rp_out, 
 
 int tile_for(int64_t r) { return r >= 1024 ? 256 : 128; }
 
+constexpr int64_t kSuperRows = 8, kSuperCols = 4;
+
 std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_config& cfg) {
   const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
   std::vector<NsChunk> chunks;
@@ -231,9 +233,14 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
           ch.gemm[kGemmGram][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
           ch.gemm[kGemmPoly][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
         }
-      for (int64_t i = 0; i < nr; ++i)
-        for (int64_t j = 0; j < nc; ++j)
-          ch.gemm[kGemmProduct][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+      // Product tiles in super-blocks of kSuperRows x kSuperCols tiles: the
+      // ~32 tiles one XCD runs at a time then share a few B and X panels in
+      // its L2 instead of streaming one B panel against 32 X panels.
+      for (int64_t jb = 0; jb < nc; jb += kSuperCols)
+        for (int64_t ib = 0; ib < nr; ib += kSuperRows)
+          for (int64_t i = ib; i < std::min(nr, ib + kSuperRows); ++i)
+            for (int64_t j = jb; j < std::min(nc, jb + kSuperCols); ++j)
+              ch.gemm[kGemmProduct][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
     }
     for (auto& op : ch.gemm)
       for (auto& gl : op) xcd_interleave(gl.items);
