@@ -249,12 +249,17 @@ __device__ __forceinline__ void w_update8(float* w, int64_t e0, int nv, const fl
 // GEMM tile C[i0.., j0..] = sum_k P[i][k] Q[j][k] on MFMA, BM x BM per
 // workgroup of WGM x WGN waves, each wave (BM/WGM) x (BM/WGN) built from
 // 32 x 32 MFMA blocks.  256-tiles run 8 waves (two per SIMD, so one wave's
-// MFMAs cover the other's memory waits); 128-tiles run 4.  The k loop stages
-// 128-byte rows (64 bf16 or 32 fp32) of P and Q through LDS, double-
-// buffered.  The 16-byte chunks of LDS row r are XOR-swizzled by
-// ((r >> 1) & 7): gfx950 serves a 128-bit LDS read in groups of 16 lanes over
-// 64 banks, and with this swizzle the 16 consecutive rows that such a group
-// reads at one logical chunk land on 16 distinct bank groups.
+// MFMAs cover the other's waits); 128-tiles run 4.
+//
+// Operand staging.  The k loop runs over stages of 64 bytes of k (32 bf16 or
+// 16 fp32) for all 2 BM rows of P and Q, NSTAGE stages deep in LDS.  Global
+// data goes straight to LDS (global_load_lds_dwordx4: each lane's 16 bytes
+// land at the wave's LDS base + 16 * lane), issued NSTAGE - 1 stages ahead of
+// its use, so no registers hold operands in flight.  A 64-byte LDS row holds
+// four 16-byte chunks; chunk c of row r sits at position c ^ ((r >> 2) & 3).
+// gfx950 serves a 128-bit LDS read in groups of 16 lanes over 64 banks, and
+// with this placement the 16 consecutive rows such a group reads at one
+// logical chunk fall on 16 distinct bank groups.
 //
 // MFMA operand layout used (both 32 x 32 variants): lane l supplies row
 // (l & 31) of P and of Q; its k values are the 16-byte chunk 2g + (l >> 5) of
@@ -274,27 +279,40 @@ __device__ __forceinline__ void w_update8(float* w, int64_t e0, int nv, const fl
 // A_ii.  This is the same arithmetic, rounded later: it avoids the
 // cancellation between a and B_ii that bf16 storage of B_ii would amplify
 // when the short side r is small.
+#define LOCAL __attribute__((address_space(3)))
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N == 0 || N == 4 || N == 8, "unsupported wait count");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
 template <typename T, int BM, int WGM, int WGN, int OP>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
     const GemmItem* __restrict__ items, int iter, int last, float ca, float cb, float cc,
     float wd) {
-  constexpr int NT = 64 * WGM * WGN;         // threads
+  constexpr int NW = WGM * WGN;
+  constexpr int NT = 64 * NW;                // threads
   constexpr int WM = BM / WGM, WN = BM / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int ROWS = 2 * BM;               // P rows then Q rows
-  constexpr int RPL = NT / 8;                // LDS rows covered by one load round
-  constexpr int LOADS = ROWS / RPL;          // 16-byte loads per thread per stage
-  constexpr int KT = 128 / int(sizeof(T));   // k elements per stage
+  constexpr int NSTAGE = 4;
+  constexpr int STAGE = ROWS * 64;           // bytes per stage
+  constexpr int BLOCKS = ROWS / 16;          // 16-row (1 KB) DMA blocks per stage
+  constexpr int DMA = BLOCKS / NW;           // DMA instructions per wave per stage
+  constexpr int KT = 64 / int(sizeof(T));    // k elements per stage
   constexpr int SLD = BM + 4;                // epilogue stage row stride (floats)
   constexpr int HALF = BM / 2;
-  constexpr int MAIN_BYTES = 2 * ROWS * 128;
+  constexpr int MAIN_BYTES = NSTAGE * STAGE;
   constexpr int STAGE_BYTES = HALF * SLD * 4;
   constexpr int SMEM = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
   static_assert(WM <= HALF && HALF % WM == 0, "a wave's rows must sit in one half");
-  static_assert(BM % RPL == 0, "load rounds must not straddle P and Q");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  u32x4_t* lds = reinterpret_cast<u32x4_t*>(smem);
+  static_assert(DMA == 4 && BLOCKS % NW == 0, "four DMA blocks per wave per stage");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  const u32x4_t* lds = reinterpret_cast<const u32x4_t*>(smem);
 
   const GemmItem it = items[blockIdx.x];
   const NsDev d = ns[it.ns];
@@ -316,25 +334,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
 
-  // Global -> LDS mapping: load round L covers LDS rows RPL L .. RPL L + RPL-1.
-  const int lrow = tid >> 3, lch = tid & 7;
-  const char* gP = reinterpret_cast<const char*>(P + (i0 + lrow) * ld) + lch * 16;
-  const char* gQ = reinterpret_cast<const char*>(Q + (j0 + lrow) * ld) + lch * 16;
-  const int64_t gstride = int64_t(RPL) * ld * int64_t(sizeof(T));
-  const int sofs = lrow * 8 + (lch ^ ((lrow >> 1) & 7));
-
-  u32x4_t stg[LOADS];
-  auto gload = [&](int kt) {
-    const int64_t kb = int64_t(kt) * 128;
+  // DMA mapping.  Instruction q of wave w fills LDS rows 16 b .. 16 b + 15 of
+  // the stage, b = w + NW q; lane l brings row 16 b + (l >> 2), logical chunk
+  // (l & 3) ^ ((l >> 4) & 3), which lands at physical chunk l & 3.
+  // Blocks q < DMA/2 are P rows, the others Q rows.
+  const int drow = 16 * wid + (lane >> 2);
+  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const char* gP = reinterpret_cast<const char*>(P + (i0 + drow) * ld) + dchunk * 16;
+  const char* gQ = reinterpret_cast<const char*>(Q + (j0 + drow) * ld) + dchunk * 16;
+  const int64_t gstride = int64_t(16 * NW) * ld * int64_t(sizeof(T));
+  auto issue = [&](int kt) {
+    const int64_t kb = int64_t(kt) * 64;
+    unsigned char* base = smem + (kt % NSTAGE) * STAGE + wid * 1024;
 #pragma unroll
-    for (int L = 0; L < LOADS; ++L) {
-      const char* src = (L < LOADS / 2) ? gP + L * gstride : gQ + (L - LOADS / 2) * gstride;
-      stg[L] = *as_global(reinterpret_cast<const u32x4_t*>(src + kb));
+    for (int q = 0; q < DMA; ++q) {
+      const char* src = (q < DMA / 2) ? gP + q * gstride : gQ + (q - DMA / 2) * gstride;
+      __builtin_amdgcn_global_load_lds((const GLOBAL void*)(src + kb),
+                                       (LOCAL void*)(base + q * NW * 1024), 16, 0, 0);
     }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int L = 0; L < LOADS; ++L) lds[buf * ROWS * 8 + L * RPL * 8 + sofs] = stg[L];
   };
 
   f32x16_t acc[FM][FN];
@@ -344,17 +361,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     for (int b = 0; b < FN; ++b) acc[a][b] = (f32x16_t)(0.0f);
 
   const int nk = int(K / KT);
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int frow = lane & 31, fsw = (lane >> 1) & 7, fhalf = lane >> 5;
-  // Fragments of k-group g (16 k values) for this wave's FM x FN MFMA blocks.
+  for (int s0 = 0; s0 < NSTAGE - 1 && s0 < nk; ++s0) issue(s0);
+
+  const int frow = lane & 31, fsw = (lane >> 2) & 3, fhalf = lane >> 5;
+  // Fragments of k-group g (16 k values) of one stage.
   auto frag = [&](const u32x4_t* sP, const u32x4_t* sQ, int g, u32x4_t* fa, u32x4_t* fb) {
     const int ch = (2 * g + fhalf) ^ fsw;
 #pragma unroll
-    for (int f = 0; f < FM; ++f) fa[f] = sP[(wm * WM + f * 32 + frow) * 8 + ch];
+    for (int f = 0; f < FM; ++f) fa[f] = sP[(wm * WM + f * 32 + frow) * 4 + ch];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) fb[f] = sQ[(wn * WN + f * 32 + frow) * 8 + ch];
+    for (int f = 0; f < FN; ++f) fb[f] = sQ[(wn * WN + f * 32 + frow) * 4 + ch];
   };
   auto mma = [&](const u32x4_t* fa, const u32x4_t* fb) {
 #pragma unroll
@@ -373,36 +389,56 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         }
       }
   };
-  // Main loop: the global loads of stage kt+1 are in flight during the
-  // MFMAs of stage kt; within a stage the LDS fragments of k-group g+1 are
-  // read while the MFMAs of group g run (two fragment register sets).  The
-  // sched_barrier(0) fences keep the compiler from sinking each fragment
-  // read next to its first use, which would expose every LDS latency.
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const u32x4_t* sP = lds + buf * ROWS * 8;
-    const u32x4_t* sQ = sP + BM * 8;
-    u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
+  // Software pipeline.  At the top of iteration kt the registers hold the
+  // fragments of both k-groups of stage kt.  The MFMAs of group 0 run; then
+  // this wave waits for its own DMA of stage kt+1 and all waves meet at a
+  // barrier (so every part of stage kt+1 is in LDS, and every wave has
+  // finished reading stage kt-1, whose buffer the DMA of stage kt+3 takes);
+  // the fragments of stage kt+1 are read while the MFMAs of group 1 of
+  // stage kt run.  LDS latency thus always hides behind a group of MFMAs.
+  // The barrier is a bare s_barrier: __syncthreads() would add a release
+  // fence that waits for every DMA in flight, i.e. for the stages
+  // prefetched ahead.
+  auto stage_ptrs = [&](int kt, const u32x4_t*& sP, const u32x4_t*& sQ) {
+    sP = lds + (kt % NSTAGE) * (STAGE / 16);
+    sQ = sP + BM * 4;
+  };
+  auto bar = [&]() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
+  {
+    if (nk > 2) wait_vmcnt<8>();
+    else if (nk == 2) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    bar();
+    const u32x4_t *sP, *sQ;
+    stage_ptrs(0, sP, sQ);
     frag(sP, sQ, 0, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
     frag(sP, sQ, 1, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    frag(sP, sQ, 2, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    frag(sP, sQ, 3, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = kt + 1 < nk;
+    const u32x4_t *sP, *sQ;
+    if (more) {
+      // stages issued after kt+1: one if kt+2 exists, else none
+      if (kt + 2 < nk) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+      bar();
+      if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
+      stage_ptrs(kt + 1, sP, sQ);
+      frag(sP, sQ, 0, a0, b0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) frag(sP, sQ, 1, a1, b1);
+  }
+  __syncthreads();
 
   // ---- epilogue -----------------------------------------------------------
   float* stage = reinterpret_cast<float*>(smem);
