@@ -246,6 +246,33 @@ __device__ __forceinline__ void w_update8(float* w, int64_t e0, int nv, const fl
   }
 }
 
+// Eight workspace values kept as loaded (bf16 stays packed) until used.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  u32x4_t u;
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    u = *as_global(reinterpret_cast<const u32x4_t*>(p));
+  }
+  __device__ __forceinline__ void unpack(float v[8]) const {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = bf16_to_f32(u[k] & 0xffffu);
+      v[2 * k + 1] = bf16_to_f32(u[k] >> 16);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = as_global(reinterpret_cast<const f32x4_t*>(p))[0];
+    b = as_global(reinterpret_cast<const f32x4_t*>(p))[1];
+  }
+  __device__ __forceinline__ void unpack(float v[8]) const {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { v[k] = a[k]; v[4 + k] = b[k]; }
+  }
+};
+
 // GEMM tile C[i0.., j0..] = sum_k P[i][k] Q[j][k] on MFMA, BM x BM per
 // workgroup of WGM x WGN waves, each wave (BM/WGM) x (BM/WGN) built from
 // 32 x 32 MFMA blocks.  256-tiles run 8 waves (two per SIMD, so one wave's
@@ -281,19 +308,25 @@ __device__ __forceinline__ void w_update8(float* w, int64_t e0, int nv, const fl
 // when the short side r is small.
 #define LOCAL __attribute__((address_space(3)))
 
+// s_waitcnt vmcnt(N) for the DMA counts the GEMM pipeline uses.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N == 0 || N == 4 || N == 8, "unsupported wait count");
+  static_assert(N == 0 || N == 2 || N == 4 || N == 8 || N == 16, "unsupported wait count");
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 }
 
 template <typename T, int BM, int WGM, int WGN, int OP>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
-    const GemmItem* __restrict__ items, int iter, int last, float ca, float cb, float cc,
+    const GemmItem* __restrict__ items, int iter, float ca, float cb, float cc,
     float wd) {
+  // OP kGemmProductLast is the product of the last round (updates W).
+  constexpr bool PROD = OP == kGemmProduct || OP == kGemmProductLast;
+  constexpr bool last = OP == kGemmProductLast;
   constexpr int NW = WGM * WGN;
   constexpr int NT = 64 * NW;                // threads
   constexpr int WM = BM / WGM, WN = BM / WGN;
@@ -310,7 +343,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   constexpr int STAGE_BYTES = HALF * SLD * 4;
   constexpr int SMEM = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
   static_assert(WM <= HALF && HALF % WM == 0, "a wave's rows must sit in one half");
-  static_assert(DMA == 4 && BLOCKS % NW == 0, "four DMA blocks per wave per stage");
+  static_assert(BLOCKS % NW == 0 && DMA % 2 == 0, "whole DMA blocks per wave, half P half Q");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   const u32x4_t* lds = reinterpret_cast<const u32x4_t*>(smem);
 
@@ -325,6 +358,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   } else if constexpr (OP == kGemmPoly) {
     P = Q = static_cast<const T*>(d.a); ld = d.rp; K = d.rp;
   } else {
+    static_assert(PROD, "unknown op");
     P = static_cast<const T*>(d.b);
     Q = static_cast<const T*>(cur ? d.xc[1] : d.xc[0]);
     ld = d.rp;
@@ -333,24 +367,39 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   const int64_t i0 = int64_t(it.ti) * BM, j0 = int64_t(it.tj) * BM;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
+  const int nk = int(K / KT);
 
   // DMA mapping.  Instruction q of wave w fills LDS rows 16 b .. 16 b + 15 of
   // the stage, b = w + NW q; lane l brings row 16 b + (l >> 2), logical chunk
   // (l & 3) ^ ((l >> 4) & 3), which lands at physical chunk l & 3.
-  // Blocks q < DMA/2 are P rows, the others Q rows.
+  // Blocks q < DMA/2 are P rows, the others Q rows.  The loads are MUBUF
+  // buffer loads into LDS: unlike the FLAT form they count only against the
+  // vector-memory counter, so waiting for LDS fragment reads does not also
+  // wait for the prefetch in flight.  Offsets past a buffer's end read 0.
   const int drow = 16 * wid + (lane >> 2);
   const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const char* gP = reinterpret_cast<const char*>(P + (i0 + drow) * ld) + dchunk * 16;
-  const char* gQ = reinterpret_cast<const char*>(Q + (j0 + drow) * ld) + dchunk * 16;
-  const int64_t gstride = int64_t(16 * NW) * ld * int64_t(sizeof(T));
+  const int64_t prow = d.rp;   // P is Xr, A or B: rp rows
+  const int64_t qrow = PROD ? d.cp : d.rp;
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(P), 0, int(prow * ld * int64_t(sizeof(T))), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(Q), 0, int(qrow * ld * int64_t(sizeof(T))), 0x00020000);
+  const unsigned offP = unsigned((i0 + drow) * ld * int64_t(sizeof(T))) + unsigned(dchunk * 16);
+  const unsigned offQ = unsigned((j0 + drow) * ld * int64_t(sizeof(T))) + unsigned(dchunk * 16);
+  const unsigned rstride = unsigned(int64_t(16 * NW) * ld * int64_t(sizeof(T)));
+  // Stages past the end are issued as a reload of the last stage: the loop
+  // body then has no branches (exact wait counts), and the buffer such a
+  // reload lands in is one no wave reads any more.
   auto issue = [&](int kt) {
-    const int64_t kb = int64_t(kt) * 64;
-    unsigned char* base = smem + (kt % NSTAGE) * STAGE + wid * 1024;
+    const unsigned kb = unsigned(min(kt, nk - 1)) * 64u;
+    LOCAL unsigned char* base = (LOCAL unsigned char*)(smem + (kt % NSTAGE) * STAGE + wid * 1024);
 #pragma unroll
     for (int q = 0; q < DMA; ++q) {
-      const char* src = (q < DMA / 2) ? gP + q * gstride : gQ + (q - DMA / 2) * gstride;
-      __builtin_amdgcn_global_load_lds((const GLOBAL void*)(src + kb),
-                                       (LOCAL void*)(base + q * NW * 1024), 16, 0, 0);
+      const bool isP = q < DMA / 2;
+      const unsigned off = (isP ? offP + unsigned(q) * rstride
+                                : offQ + unsigned(q - DMA / 2) * rstride) + kb;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isP ? rP : rQ, (LOCAL void*)(base + q * NW * 1024),
+                                               16, off, 0, 0, 0);
     }
   };
 
@@ -360,8 +409,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
 #pragma unroll
     for (int b = 0; b < FN; ++b) acc[a][b] = (f32x16_t)(0.0f);
 
-  const int nk = int(K / KT);
-  for (int s0 = 0; s0 < NSTAGE - 1 && s0 < nk; ++s0) issue(s0);
+  for (int s0 = 0; s0 < NSTAGE - 1; ++s0) issue(s0);
 
   const int frow = lane & 31, fsw = (lane >> 2) & 3, fhalf = lane >> 5;
   // Fragments of k-group g (16 k values) of one stage.
@@ -409,38 +457,41 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   };
   u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
   {
-    if (nk > 2) wait_vmcnt<8>();
-    else if (nk == 2) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<2 * DMA>();          // stage 0 is in; stages 1, 2 may be in flight
     bar();
     const u32x4_t *sP, *sQ;
     stage_ptrs(0, sP, sQ);
     frag(sP, sQ, 0, a0, b0);
     frag(sP, sQ, 1, a1, b1);
   }
+  // Every iteration issues exactly DMA loads, so after the waits below the
+  // only DMA in flight is that of stage kt + 2.  The fragment reads of stage
+  // nk (past the end) read a reloaded buffer and are never used.
   for (int kt = 0; kt < nk; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
     mma(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    const bool more = kt + 1 < nk;
+    wait_vmcnt<DMA>();
+    bar();
+    issue(kt + NSTAGE - 1);
     const u32x4_t *sP, *sQ;
-    if (more) {
-      // stages issued after kt+1: one if kt+2 exists, else none
-      if (kt + 2 < nk) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-      bar();
-      if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
-      stage_ptrs(kt + 1, sP, sQ);
-      frag(sP, sQ, 0, a0, b0);
-    }
+    stage_ptrs(kt + 1, sP, sQ);
+    frag(sP, sQ, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
     mma(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    if (more) frag(sP, sQ, 1, a1, b1);
+    frag(sP, sQ, 1, a1, b1);
   }
+  wait_vmcnt<0>();
   __syncthreads();
 
   // ---- epilogue -----------------------------------------------------------
+  // Stage layout: value (r, c) of a half tile sits at r * SLD + (c ^ sw(r)),
+  // sw(r) = ((r >> 4) & 7) << 2.  The transposed pass reads a column run
+  // r = 8 ch + u (ch = 0..15) at fixed c; with the swizzle those 16 reads hit
+  // 16 distinct banks.  A row run of 8 values starting at a multiple of 8
+  // stays inside one aligned group of 8, with its two 4-value halves swapped
+  // when bit 2 of sw(r) is set.
   float* stage = reinterpret_cast<float*>(smem);
   const bool diag_tile = it.ti == it.tj;
   T* xr = static_cast<T*>(d.xr);
@@ -448,101 +499,180 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   float* w = mats[d.mat].w;
   const float wkeep = 1.0f - d.lr * wd;
   bool mirror;
-  if constexpr (OP == kGemmProduct) mirror = !last || d.tall;
+  if constexpr (PROD) mirror = !last || d.tall;
   else mirror = !diag_tile;
+  auto sw = [](int r) { return ((r >> 4) & 7) << 2; };
+  constexpr int CPR = BM / 8;                  // 8-value chunks per tile row
+  constexpr int DIT = HALF * CPR / NT;         // direct-pass chunks per thread
+  constexpr int CPC = HALF / 8;                // 8-value chunks per mirrored row
+  constexpr int MIT = BM * CPC / NT;           // mirror-pass chunks per thread
+  static_assert(DIT * NT == HALF * CPR && MIT * NT == BM * CPC, "whole passes");
+  // The direct pass needs operand reads per chunk (A for B; X for the
+  // product, plus W for the last product of a wide matrix).  They are issued in
+  // batches of PB chunks, the first batch before the accumulators are
+  // parked, so their latency overlaps the staging and its barrier.
+  const bool need_aux = OP == kGemmPoly || PROD;
+  const bool aux_is_w = last && !d.tall;     // also the W values to update
+  // Batch size: as many chunks in flight as registers allow without spills
+  // (8 packed bf16 chunks; 4 for fp32 and for the last product, which also
+  // carries W).
+  constexpr int PBMAX = (last || sizeof(T) == 4) ? 4 : 8;
+  constexpr int PB = DIT < PBMAX ? DIT : PBMAX;
+  constexpr int NB = DIT / PB;
+  static_assert(NB * PB == DIT, "whole batches");
 
 #pragma unroll 1
   for (int half = 0; half < 2; ++half) {
-    if ((wm * WM) / HALF == half) {
+    const int64_t ib0 = i0 + int64_t(half) * HALF;
+    Raw8<T> ra[PB];
+    Raw8<float> rw[PB];
+    int rw_nv[PB];
+    auto prefetch = [&](int bt) {
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int idx = tid + (bt * PB + q) * NT;
+        const int r = idx / CPR, ch = idx % CPR;
+        const int64_t i = ib0 + r, j = j0 + ch * 8;
+        if constexpr (OP == kGemmPoly) ra[q].load(static_cast<const T*>(d.a) + i * d.rp + j);
+        else ra[q].load(xr + i * d.cp + j);
+        if (aux_is_w) {
+          const int nv = (i < d.r) ? int(max<int64_t>(0, min<int64_t>(8, d.c - j))) : 0;
+          const int64_t e0 = i * d.ld + d.col0 + j;
+          rw_nv[q] = nv;
+          if (nv == 8 && (e0 & 3) == 0) {
+            rw[q].load(w + e0);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              rw[q].a[u] = (u < nv) ? as_global(w)[e0 + u] : 0.f;
+              rw[q].b[u] = (u + 4 < nv) ? as_global(w)[e0 + 4 + u] : 0.f;
+            }
+          }
+        }
+      }
+    };
+    if (need_aux) prefetch(0);
+    if (wm * WM >= half * HALF && wm * WM < (half + 1) * HALF) {
       const int rbase = wm * WM - half * HALF;
 #pragma unroll
       for (int fa = 0; fa < FM; ++fa)
 #pragma unroll
         for (int fb = 0; fb < FN; ++fb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            stage[(rbase + fa * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3)) * SLD + wn * WN + fb * 32 +
-                  frow] = acc[fa][fb][v];
+          for (int v = 0; v < 16; ++v) {
+            const int r = rbase + fa * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3);
+            const int c = wn * WN + fb * 32 + frow;
+            stage[r * SLD + (c ^ sw(r))] = acc[fa][fb][v];
+          }
     }
     __syncthreads();
-    const int64_t ib0 = i0 + int64_t(half) * HALF;
     // rows of the tile: C[i][j .. j+7]
-    constexpr int CPR = BM / 8;
-    for (int idx = tid; idx < HALF * CPR; idx += NT) {
-      const int r = idx / CPR, ch = idx % CPR;
-      const int64_t i = ib0 + r, j = j0 + ch * 8;
-      float* sv = stage + r * SLD + ch * 8;
-      float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = sv[u];
-      const bool has_diag = diag_tile && i >= j && i < j + 8;
-      const int du = int(i - j);
-      if constexpr (OP == kGemmGram) {
-        if (has_diag) {
-          float dv = 0.f;
+    for (int bt = 0; bt < NB; ++bt) {
+      if (bt > 0 && need_aux) prefetch(bt);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) dv = (u == du) ? v[u] : dv;
-          d.adiag[i] = dv;
-        }
-        store8(static_cast<T*>(d.a) + i * d.rp + j, v);
-      } else if constexpr (OP == kGemmPoly) {
-        float av[8];
-        load8(static_cast<const T*>(d.a) + i * d.rp + j, av);
-        float dval = 0.f;
-        if (has_diag) {
-          float acc_ii = 0.f, a_ii = 0.f;
+      for (int q = 0; q < PB; ++q) {
+        const int idx = tid + (bt * PB + q) * NT;
+        const int r = idx / CPR, ch = idx % CPR;
+        const int64_t i = ib0 + r, j = j0 + ch * 8;
+        const int swz = sw(r);
+        f32x4_t* sv = reinterpret_cast<f32x4_t*>(stage + r * SLD + ((ch * 8) ^ (swz & ~7)));
+        const bool flip = (swz & 4) != 0;
+        const f32x4_t lo = flip ? sv[1] : sv[0], hi = flip ? sv[0] : sv[1];
+        float v[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            acc_ii = (u == du) ? v[u] : acc_ii;
-            a_ii = (u == du) ? av[u] : a_ii;
+        for (int u = 0; u < 4; ++u) { v[u] = lo[u]; v[4 + u] = hi[u]; }
+        const bool has_diag = diag_tile && i >= j && i < j + 8;
+        const int du = int(i - j);
+        bool writeback = false;
+        if constexpr (OP == kGemmGram) {
+          if (has_diag) {
+            float dv = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dv = (u == du) ? v[u] : dv;
+            d.adiag[i] = dv;
           }
-          const float ad = d.adiag[i];
-          const float aa = acc_ii + ad * ad - a_ii * a_ii;
-          dval = fmaf(cb, ad, cc * aa);
-          d.bdiag[i] = dval;
-        }
+          store8(static_cast<T*>(d.a) + i * d.rp + j, v);
+        } else if constexpr (OP == kGemmPoly) {
+          float av[8];
+          ra[q].unpack(av);
+          if (has_diag) {
+            float acc_ii = 0.f, a_ii = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (has_diag && u == du) ? 0.f : fmaf(cc, v[u], cb * av[u]);
-        store8(static_cast<T*>(d.b) + i * d.rp + j, v);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) sv[u] = v[u];
-      } else {
-        float xv[8];
-        load8(xr + i * d.cp + j, xv);
-        const float mlt = ca + d.bdiag[i];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = fmaf(mlt, xv[u], v[u]);
-        if (!last) {
-          store8(xr + i * d.cp + j, v);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) sv[u] = v[u];
-        } else if (!d.tall) {
-          if (i < d.r) {
-            const int nv = int(max<int64_t>(0, min<int64_t>(8, d.c - j)));
-            if (nv > 0) w_update8(w, i * d.ld + d.col0 + j, nv, v, d.lr, wkeep);
+            for (int u = 0; u < 8; ++u) {
+              acc_ii = (u == du) ? v[u] : acc_ii;
+              a_ii = (u == du) ? av[u] : a_ii;
+            }
+            const float ad = d.adiag[i];
+            const float aa = acc_ii + ad * ad - a_ii * a_ii;
+            d.bdiag[i] = fmaf(cb, ad, cc * aa);
           }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            v[u] = (has_diag && u == du) ? 0.f : fmaf(cc, v[u], cb * av[u]);
+          store8(static_cast<T*>(d.b) + i * d.rp + j, v);
+          writeback = true;
         } else {
+          const float mlt = ca + d.bdiag[i];
+          if constexpr (!last) {
+            float xv[8];
+            ra[q].unpack(xv);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) sv[u] = v[u];
+            for (int u = 0; u < 8; ++u) v[u] = fmaf(mlt, xv[u], v[u]);
+            store8(xr + i * d.cp + j, v);
+            writeback = true;
+          } else if (!d.tall) {
+            float xv[8], wv[8];
+            ra[q].unpack(xv);
+            rw[q].unpack(wv);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = fmaf(-d.lr, fmaf(mlt, xv[u], v[u]), wv[u] * wkeep);
+            const int nv = rw_nv[q];
+            const int64_t e0 = i * d.ld + d.col0 + j;
+            GLOBAL float* gw = as_global(w) + e0;
+            if (nv == 8 && (e0 & 3) == 0) {
+              reinterpret_cast<GLOBAL f32x4_t*>(gw)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+              reinterpret_cast<GLOBAL f32x4_t*>(gw)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+            } else {
+#pragma unroll
+              for (int u = 0; u < 8; ++u)
+                if (u < nv) gw[u] = v[u];
+            }
+          } else {
+            float xv[8];
+            ra[q].unpack(xv);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = fmaf(mlt, xv[u], v[u]);
+            writeback = true;
+          }
+        }
+        if (writeback) {
+          const f32x4_t a4 = {v[0], v[1], v[2], v[3]}, b4 = {v[4], v[5], v[6], v[7]};
+          sv[flip ? 1 : 0] = a4;
+          sv[flip ? 0 : 1] = b4;
         }
       }
     }
     __syncthreads();
     // columns of the tile: C[i .. i+7][j] written as row j of the transpose
     if (mirror) {
-      constexpr int CPC = HALF / 8;
-      for (int idx = tid; idx < BM * CPC; idx += NT) {
+#pragma unroll
+      for (int q = 0; q < MIT; ++q) {
+        const int idx = tid + q * NT;
         const int jj = idx / CPC, ch = idx % CPC;
         const int64_t j = j0 + jj, i = ib0 + ch * 8;
         float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = stage[(ch * 8 + u) * SLD + jj];
+        for (int u = 0; u < 8; ++u) {
+          const int r = ch * 8 + u;
+          v[u] = stage[r * SLD + (jj ^ sw(r))];
+        }
         if constexpr (OP == kGemmGram) {
           store8(static_cast<T*>(d.a) + j * d.rp + i, v);
         } else if constexpr (OP == kGemmPoly) {
           store8(static_cast<T*>(d.b) + j * d.rp + i, v);
         } else {
-          if (!last) {
+          if constexpr (!last) {
             store8(xcn + j * d.rp + i, v);
           } else if (j < d.c) {
             const int nv = int(max<int64_t>(0, min<int64_t>(8, d.r - i)));
@@ -555,26 +685,35 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   }
 }
 
-// 256-tiles: 8 waves in a 2 x 4 grid; 128-tiles: 4 waves in 2 x 2.
-template <int BM> struct WaveGrid;
-template <> struct WaveGrid<256> { static constexpr int M = 2, N = 4; };
-template <> struct WaveGrid<128> { static constexpr int M = 2, N = 2; };
+// Wave grids, chosen by timing on gfx950 (18 problems of 2048 x 8192): all
+// tiles run 4 waves in a 2 x 2 grid, one wave per SIMD; a 256-tile wave
+// holds its 128 x 128 accumulators in the 256 AGPRs.
+template <int BM, int OP> struct WaveGrid { static constexpr int M = 2, N = 2; };
+
+template <typename T, int BM, int OP>
+void launch_gemm_op(hipStream_t s, const MatDev* mats, const NsDev* ns, const GemmItem* items,
+                    int64_t nitems, int iter, float a, float b, float c, float wd) {
+  constexpr int GM = WaveGrid<BM, OP>::M, GN = WaveGrid<BM, OP>::N;
+  ns_gemm_kernel<T, BM, GM, GN, OP><<<dim3(static_cast<unsigned>(nitems)), dim3(64 * GM * GN), 0, s>>>(
+      mats, ns, items, iter, a, b, c, wd);
+}
 
 template <typename T, int BM>
 hipError_t launch_gemm_t(hipStream_t s, const MatDev* mats, const NsDev* ns,
                          const GemmItem* items, int64_t nitems, int op, int iter, int last,
                          float a, float b, float c, float wd) {
-  constexpr int GM = WaveGrid<BM>::M, GN = WaveGrid<BM>::N;
-  const dim3 grid(static_cast<unsigned>(nitems)), block(64 * GM * GN);
   switch (op) {
     case kGemmGram:
-      ns_gemm_kernel<T, BM, GM, GN, kGemmGram><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      launch_gemm_op<T, BM, kGemmGram>(s, mats, ns, items, nitems, iter, a, b, c, wd);
       break;
     case kGemmPoly:
-      ns_gemm_kernel<T, BM, GM, GN, kGemmPoly><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      launch_gemm_op<T, BM, kGemmPoly>(s, mats, ns, items, nitems, iter, a, b, c, wd);
       break;
     default:
-      ns_gemm_kernel<T, BM, GM, GN, kGemmProduct><<<grid, block, 0, s>>>(mats, ns, items, iter, last, a, b, c, wd);
+      if (last)
+        launch_gemm_op<T, BM, kGemmProductLast>(s, mats, ns, items, nitems, iter, a, b, c, wd);
+      else
+        launch_gemm_op<T, BM, kGemmProduct>(s, mats, ns, items, nitems, iter, a, b, c, wd);
       break;
   }
   return hipGetLastError();

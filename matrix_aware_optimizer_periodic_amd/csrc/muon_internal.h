@@ -114,6 +114,7 @@ hipError_t launch_adamw(hipStream_t s, const AdamDev* t, const AdamChunk* chunks
 hipError_t launch_patch(hipStream_t s, MatDev* mats, AdamDev* adams, const PatchArgs& args);
 
 constexpr int kGemmGram = 0, kGemmPoly = 1, kGemmProduct = 2;
+constexpr int kGemmProductLast = 3;  // kernel variant only: product that updates W
 constexpr int kRowChunkElems = 1024;   // elements per row-kernel chunk (256 thr x 4)
 constexpr int kColTileRows = 512;      // tall RowNorm tile rows
 constexpr int kColTileCols = 256;      // tall RowNorm tile columns
