@@ -187,14 +187,13 @@ typedef enum muon_kernel_class {
   MUON_K_ROWNORM_ROWS = 0,   /* RowNorm step, row-normalised matrices        */
   MUON_K_ROWNORM_COLS1 = 1,  /* RowNorm step, tall: momentum + column sums   */
   MUON_K_ROWNORM_COLS2 = 2,  /* RowNorm step, tall: scale + weight update    */
-  MUON_K_NS_MOMENTUM = 3,    /* refresh: momentum + Frobenius partial sums   */
+  MUON_K_NS_PREP = 3,        /* refresh: momentum, Frobenius partials, X0    */
   MUON_K_NS_SCALE = 4,       /* refresh: 1 / (||M||_F + eps)                 */
-  MUON_K_NS_CAST = 5,        /* refresh: X0 in both layouts                  */
-  MUON_K_NS_GRAM = 6,        /* refresh: A = X X^T                           */
-  MUON_K_NS_POLY = 7,        /* refresh: B = b A + c A A                     */
-  MUON_K_NS_PRODUCT = 8,     /* refresh: X = a X + B X (last: W update)      */
-  MUON_K_ADAMW = 9,          /* AdamW on the non-matrix tensors              */
-  MUON_K_COUNT = 10
+  MUON_K_NS_GRAM = 5,        /* refresh: A = X X^T                           */
+  MUON_K_NS_POLY = 6,        /* refresh: B = b A + c A A                     */
+  MUON_K_NS_PRODUCT = 7,     /* refresh: X = a X + B X (last: W update)      */
+  MUON_K_ADAMW = 8,          /* AdamW on the non-matrix tensors              */
+  MUON_K_COUNT = 9
 } muon_kernel_class;
 
 /* While enabled (enable != 0), muon_step records a HIP event before and

@@ -26,8 +26,8 @@ EXPORTED = ("muon_config_default", "muon_state_bytes", "muon_init", "muon_step",
             "muon_timing_enable", "muon_timing_read")
 
 # muon_kernel_class, in enum order
-KERNEL_CLASSES = ("rownorm_rows", "rownorm_cols1", "rownorm_cols2", "ns_momentum", "ns_scale",
-                  "ns_cast", "ns_gram", "ns_poly", "ns_product", "adamw")
+KERNEL_CLASSES = ("rownorm_rows", "rownorm_cols1", "rownorm_cols2", "ns_prep", "ns_scale",
+                  "ns_gram", "ns_poly", "ns_product", "adamw")
 
 
 class MuonTensor(ctypes.Structure):

@@ -75,25 +75,38 @@ __device__ __forceinline__ float load_g(const void* g, int gdt, int64_t idx) {
 }
 
 // ---------------------------------------------------------------------------
-// Momentum over one NS problem's stored block, kMomRowsPerPart rows per
-// workgroup, plus that slab's sum of squares (one partial per workgroup).
-__global__ __launch_bounds__(kThreads) void ns_momentum_kernel(
+// Refresh-step preparation, one 64 x 64 tile of the padded stored block per
+// workgroup: M <- beta M + G for the tile's valid elements, the tile's sum of
+// squares (one partial per tile), and the new M, unscaled, cast to the
+// workspace type in both layouts (Xr and Xc[0]); padding is written as 0.
+// The pre-normalisation factor s = 1 / (||M||_F + eps) is applied by the
+// first Newton-Schulz round instead (A = s^2 X X^T, X_1 = s (a X + B X)),
+// which saves a second pass over M.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void ns_prep_kernel(
     const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
     const TileItem* __restrict__ items, float beta) {
+  __shared__ float tile[kPrepTile][kPrepTile + 1];
   __shared__ float red[4];
   const TileItem it = items[blockIdx.x];
   const NsDev d = ns[it.id];
   const MatDev mt = mats[d.mat];
-  const int64_t r0 = int64_t(it.ti) * d.rows_per_part;
-  const int64_t r1 = min(d.rows, r0 + d.rows_per_part);
+  const int64_t p0 = int64_t(it.ti) * kPrepTile, q0 = int64_t(it.tj) * kPrepTile;
+  T* dst = static_cast<T*>(d.tall ? d.xc[0] : d.xr);     // stored orientation
+  const int64_t ldd = d.tall ? d.rp : d.cp;
+  T* dstt = static_cast<T*>(d.tall ? d.xr : d.xc[0]);    // transposed
+  const int64_t ldt = d.tall ? d.cp : d.rp;
+  const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
+  const bool vec = ((d.ld | d.col0) & 3) == 0 && q0 + kPrepTile <= d.cols;
   float ss = 0.f;
-  const bool vec = ((d.ld | d.col0 | d.cols) & 3) == 0;
-  if (vec) {
-    const int64_t n4 = d.cols >> 2;
-    for (int64_t r = r0; r < r1; ++r) {
-      const int64_t base = r * d.ld + d.col0;
-      for (int64_t q = threadIdx.x; q < n4; q += kThreads) {
-        const int64_t e = base + 4 * q;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int lr = tr + 16 * pass;
+    const int64_t p = p0 + lr;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (p < d.rows) {
+      const int64_t e = p * d.ld + d.col0 + q0 + tc;
+      if (vec) {
         float4 g;
         if (mt.gdt == 1) {
           const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(mt.g) + e);
@@ -106,62 +119,21 @@ __global__ __launch_bounds__(kThreads) void ns_momentum_kernel(
         m = make_float4(fmaf(beta, m.x, g.x), fmaf(beta, m.y, g.y), fmaf(beta, m.z, g.z),
                         fmaf(beta, m.w, g.w));
         *reinterpret_cast<float4*>(mt.mom + e) = m;
-        ss += m.x * m.x + m.y * m.y + m.z * m.z + m.w * m.w;
-      }
-    }
-  } else {
-    for (int64_t r = r0; r < r1; ++r) {
-      const int64_t base = r * d.ld + d.col0;
-      for (int64_t q = threadIdx.x; q < d.cols; q += kThreads) {
-        const int64_t e = base + q;
-        const float m = fmaf(beta, mt.mom[e], load_g(mt.g, mt.gdt, e));
-        mt.mom[e] = m;
-        ss += m * m;
-      }
-    }
-  }
-  const float tot = block_sum(ss, red);
-  if (threadIdx.x == 0) d.part[it.ti] = tot;
-}
-
-// 1 / (||M||_F + eps) per NS problem, partials added in a fixed order.
-__global__ __launch_bounds__(kThreads) void ns_scale_kernel(NsDev* __restrict__ ns, float eps) {
-  __shared__ float red[4];
-  const NsDev d = ns[blockIdx.x];
-  float s = 0.f;
-  for (int k = threadIdx.x; k < d.nparts; k += kThreads) s += d.part[k];
-  const float tot = block_sum(s, red);
-  if (threadIdx.x == 0) d.scale[0] = 1.0f / (sqrtf(tot) + eps);
-}
-
-// X0 = M * scale, cast to the workspace type and written in both layouts.
-// One 64 x 64 tile of the padded stored block per workgroup; elements
-// outside the logical block are written as zeros.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void ns_cast_kernel(
-    const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
-    const TileItem* __restrict__ items) {
-  __shared__ float tile[kPrepTile][kPrepTile + 1];
-  const TileItem it = items[blockIdx.x];
-  const NsDev d = ns[it.id];
-  const float* __restrict__ mom = mats[d.mat].mom;
-  const float sc = d.scale[0];
-  const int64_t p0 = int64_t(it.ti) * kPrepTile, q0 = int64_t(it.tj) * kPrepTile;
-  // direct copy (stored orientation) and transposed copy
-  T* dst = static_cast<T*>(d.tall ? d.xc[0] : d.xr);
-  const int64_t ldd = d.tall ? d.rp : d.cp;
-  T* dstt = static_cast<T*>(d.tall ? d.xr : d.xc[0]);
-  const int64_t ldt = d.tall ? d.cp : d.rp;
-  const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
+        v[0] = m.x; v[1] = m.y; v[2] = m.z; v[3] = m.w;
+      } else {
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int lr = tr + 16 * pass;
-    const int64_t p = p0 + lr;
-    float v[4];
+        for (int u = 0; u < 4; ++u) {
+          if (q0 + tc + u < d.cols) {
+            const float m = fmaf(beta, mt.mom[e + u], load_g(mt.g, mt.gdt, e + u));
+            mt.mom[e + u] = m;
+            v[u] = m;
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t q = q0 + tc + u;
-      v[u] = (p < d.rows && q < d.cols) ? mom[p * d.ld + d.col0 + q] * sc : 0.f;
+      ss += v[u] * v[u];
       tile[lr][tc + u] = v[u];
     }
     T* o = dst + p * ldd + q0 + tc;
@@ -173,7 +145,8 @@ __global__ __launch_bounds__(kThreads) void ns_cast_kernel(
       *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
   }
-  __syncthreads();
+  const float tot = block_sum(ss, red);   // contains the barrier the transpose needs
+  if (threadIdx.x == 0) d.part[int64_t(it.ti) * (d.tall ? d.rp : d.cp) / kPrepTile + it.tj] = tot;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int lq = tr + 16 * pass;
@@ -189,6 +162,16 @@ __global__ __launch_bounds__(kThreads) void ns_cast_kernel(
       *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
   }
+}
+
+// s = 1 / (||M||_F + eps) per NS problem, partials added in a fixed order.
+__global__ __launch_bounds__(kThreads) void ns_scale_kernel(NsDev* __restrict__ ns, float eps) {
+  __shared__ float red[4];
+  const NsDev d = ns[blockIdx.x];
+  float s = 0.f;
+  for (int k = threadIdx.x; k < d.nparts; k += kThreads) s += d.part[k];
+  const float tot = block_sum(s, red);
+  if (threadIdx.x == 0) d.scale[0] = 1.0f / (sqrtf(tot) + eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -502,6 +485,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   if constexpr (PROD) mirror = !last || d.tall;
   else mirror = !diag_tile;
   auto sw = [](int r) { return ((r >> 4) & 7) << 2; };
+  // Round 0 works on the unscaled M: A = s^2 (M M^T), X_1 = s (a M + B M).
+  const float s0 = iter == 0 ? d.scale[0] : 1.0f;
+  const float gscale = s0 * s0, pscale = s0;
   constexpr int CPR = BM / 8;                  // 8-value chunks per tile row
   constexpr int DIT = HALF * CPR / NT;         // direct-pass chunks per thread
   constexpr int CPC = HALF / 8;                // 8-value chunks per mirrored row
@@ -586,6 +572,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         const int du = int(i - j);
         bool writeback = false;
         if constexpr (OP == kGemmGram) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] *= gscale;
           if (has_diag) {
             float dv = 0.f;
 #pragma unroll
@@ -618,7 +606,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
             float xv[8];
             ra[q].unpack(xv);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = fmaf(mlt, xv[u], v[u]);
+            for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
             store8(xr + i * d.cp + j, v);
             writeback = true;
           } else if (!d.tall) {
@@ -626,7 +614,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
             ra[q].unpack(xv);
             rw[q].unpack(wv);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = fmaf(-d.lr, fmaf(mlt, xv[u], v[u]), wv[u] * wkeep);
+            for (int u = 0; u < 8; ++u)
+              v[u] = fmaf(-d.lr, pscale * fmaf(mlt, xv[u], v[u]), wv[u] * wkeep);
             const int nv = rw_nv[q];
             const int64_t e0 = i * d.ld + d.col0 + j;
             GLOBAL float* gw = as_global(w) + e0;
@@ -642,7 +631,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
             float xv[8];
             ra[q].unpack(xv);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = fmaf(mlt, xv[u], v[u]);
+            for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
             writeback = true;
           }
         }
@@ -668,6 +657,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           v[u] = stage[r * SLD + (jj ^ sw(r))];
         }
         if constexpr (OP == kGemmGram) {
+          // the direct pass does not write its scaled values back to the stage
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] *= gscale;
           store8(static_cast<T*>(d.a) + j * d.rp + i, v);
         } else if constexpr (OP == kGemmPoly) {
           store8(static_cast<T*>(d.b) + j * d.rp + i, v);
@@ -721,27 +713,20 @@ hipError_t launch_gemm_t(hipStream_t s, const MatDev* mats, const NsDev* ns,
 
 }  // namespace
 
-hipError_t launch_ns_momentum(hipStream_t s, const MatDev* mats, const NsDev* ns,
-                              const TileItem* items, int64_t nitems, float beta) {
+hipError_t launch_ns_prep(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                          const TileItem* items, int64_t nitems, int prec, float beta) {
   if (nitems <= 0) return hipSuccess;
-  ns_momentum_kernel<<<dim3(static_cast<unsigned>(nitems)), dim3(kThreads), 0, s>>>(mats, ns, items, beta);
+  const dim3 grid(static_cast<unsigned>(nitems)), block(kThreads);
+  if (prec == 0)
+    ns_prep_kernel<uint16_t><<<grid, block, 0, s>>>(mats, ns, items, beta);
+  else
+    ns_prep_kernel<float><<<grid, block, 0, s>>>(mats, ns, items, beta);
   return hipGetLastError();
 }
 
 hipError_t launch_ns_scale(hipStream_t s, NsDev* ns_dev, int32_t count, float eps) {
   if (count <= 0) return hipSuccess;
   ns_scale_kernel<<<dim3(count), dim3(kThreads), 0, s>>>(ns_dev, eps);
-  return hipGetLastError();
-}
-
-hipError_t launch_ns_cast(hipStream_t s, const MatDev* mats, const NsDev* ns,
-                          const TileItem* items, int64_t nitems, int prec) {
-  if (nitems <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(nitems)), block(kThreads);
-  if (prec == 0)
-    ns_cast_kernel<uint16_t><<<grid, block, 0, s>>>(mats, ns, items);
-  else
-    ns_cast_kernel<float><<<grid, block, 0, s>>>(mats, ns, items);
   return hipGetLastError();
 }
 

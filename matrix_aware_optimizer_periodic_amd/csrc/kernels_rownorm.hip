@@ -144,11 +144,13 @@ __global__ __launch_bounds__(kThreads) void rownorm_rows_kernel(
 // Phase 1 writes the new momentum and one partial column sum of squares per
 // (row tile, column); phase 2 adds the partials of all row tiles in order,
 // then scales and updates W.
+// Phase 2 visits the tiles in reverse order, so the momentum phase 1 wrote
+// last (most likely still in the Infinity Cache) is read first.
 template <int PHASE>
 __global__ __launch_bounds__(kThreads) void rownorm_cols_kernel(
     const MatDev* __restrict__ mats, const TileItem* __restrict__ tiles, StepScalars sc) {
   __shared__ float red[4][kColTileCols];
-  const TileItem it = tiles[blockIdx.x];
+  const TileItem it = tiles[PHASE == 1 ? blockIdx.x : gridDim.x - 1 - blockIdx.x];
   const MatDev d = mats[it.id];
   const int64_t m = d.rows, n = d.cols;
   const int64_t r0 = int64_t(it.ti) * kColTileRows;

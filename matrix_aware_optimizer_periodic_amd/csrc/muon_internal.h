@@ -52,14 +52,12 @@ struct NsDev {
   void* xc[2];       // cp x rp, X^T row-major, ping-pong
   void* a;           // rp x rp, X X^T
   void* b;           // rp x rp, b A + c A A
-  float* part;       // Frobenius partial sums, nparts
-  float* scale;      // 1 / (||M||_F + eps), one float
+  float* part;       // Frobenius partial sums, one per prep tile (nparts)
+  float* scale;      // s = 1 / (||M||_F + eps), one float
   float* adiag;      // rp: diagonal of A kept in fp32
   float* bdiag;      // rp: diagonal of B kept in fp32 (stored B has 0 there)
   int32_t nparts;
-  int32_t rows_per_part;
   float lr;          // learning rate applied by the final product
-  float pad;
 };
 
 // A GEMM output tile of one NsDev.
@@ -100,11 +98,10 @@ hipError_t launch_rownorm_rows(hipStream_t s, const MatDev* mats, const int32_t*
 // phase 2 (norms + weight update), one workgroup per tile.
 hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem* tiles,
                                int64_t ntiles, int phase, StepScalars sc);
-hipError_t launch_ns_momentum(hipStream_t s, const MatDev* mats, const NsDev* ns,
-                              const TileItem* items, int64_t nitems, float beta);
+// Refresh prep: momentum, Frobenius partials, unscaled X0 in both layouts.
+hipError_t launch_ns_prep(hipStream_t s, const MatDev* mats, const NsDev* ns,
+                          const TileItem* items, int64_t nitems, int prec, float beta);
 hipError_t launch_ns_scale(hipStream_t s, NsDev* ns_dev, int32_t count, float eps);
-hipError_t launch_ns_cast(hipStream_t s, const MatDev* mats, const NsDev* ns,
-                          const TileItem* items, int64_t nitems, int prec);
 hipError_t launch_ns_gemm(hipStream_t s, const MatDev* mats, const NsDev* ns,
                           const GemmItem* items, int64_t nitems, int op, int tile,
                           int prec, int iter, int last, float a, float b, float c, float wd);
@@ -119,7 +116,6 @@ constexpr int kRowChunkElems = 1024;   // elements per row-kernel chunk (256 thr
 constexpr int kColTileRows = 512;      // tall RowNorm tile rows
 constexpr int kColTileCols = 256;      // tall RowNorm tile columns
 constexpr int kPrepTile = 64;          // NS5 cast/transpose tile
-constexpr int kMomRowsPerPart = 8;     // rows per Frobenius partial
 constexpr int kAdamChunk = 4096;       // elements per AdamW workgroup
 
 }  // namespace muon

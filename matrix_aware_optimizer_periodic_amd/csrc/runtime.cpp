@@ -50,9 +50,9 @@ struct GemmList {
 struct NsChunk {
   std::vector<NsDev> ns;          // device pointers filled once base is known
   std::vector<size_t> ws_off;     // per problem: workspace offset (relative to ws base)
-  std::vector<TileItem> mom_items, cast_items;
+  std::vector<TileItem> prep_items;
   GemmList gemm[3][2];            // [op][tile == 256]
-  size_t off_ns = 0, off_mom = 0, off_cast = 0;
+  size_t off_ns = 0, off_prep = 0;
   size_t ws_bytes = 0;
 };
 
@@ -173,7 +173,7 @@ size_t problem_ws_bytes(const Problem& p, int tile, size_t es, int64_t* rp_out, 
                         int32_t* nparts_out) {
   const int64_t r = std::min(p.rows, p.cols), c = std::max(p.rows, p.cols);
   const int64_t rp = ceil_div(r, tile) * tile, cp = ceil_div(c, tile) * tile;
-  const int32_t nparts = static_cast<int32_t>(ceil_div(p.rows, kMomRowsPerPart));
+  const int32_t nparts = static_cast<int32_t>((rp / kPrepTile) * (cp / kPrepTile));
   *rp_out = rp; *cp_out = cp; *nparts_out = nparts;
   size_t b = 0;
   b += align_up(size_t(rp) * cp * es, kAlign);          // xr
@@ -189,6 +189,9 @@ int tile_for(int64_t r) { return r >= 1024 ? 256 : 128; }
 
 constexpr int64_t kSuperRows = 8, kSuperCols = 4;
 
+// Tall RowNorm matrices run phase 1 and phase 2 group by group, each group's
+// new momentum (written by phase 1, re-read by phase 2) small enough to stay
+// in the 256 MB Infinity Cache between the two launches.
 std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_config& cfg) {
   const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
   std::vector<NsChunk> chunks;
@@ -209,7 +212,6 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
     d.rows = p.rows; d.cols = p.cols; d.col0 = p.col0; d.ld = p.ld;
     d.r = r; d.c = std::max(p.rows, p.cols); d.rp = rp; d.cp = cp;
     d.nparts = nparts;
-    d.rows_per_part = kMomRowsPerPart;
     d.lr = p.lr;
     cur.ws_off.push_back(cur.ws_bytes);
     cur.ws_bytes += wb;
@@ -222,11 +224,12 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
       const NsDev& d = ch.ns[k];
       const int tile = tile_for(d.r);
       const int t256 = tile == 256 ? 1 : 0;
-      for (int32_t q = 0; q < d.nparts; ++q) ch.mom_items.push_back(TileItem{k, int16_t(q), 0});
+      // prep tiles over the padded stored block; tile (a, b) owns partial
+      // a * (stored padded cols / 64) + b
       const int64_t sp = d.tall ? d.cp : d.rp, sq = d.tall ? d.rp : d.cp;
       for (int64_t a = 0; a < sp / kPrepTile; ++a)
         for (int64_t b = 0; b < sq / kPrepTile; ++b)
-          ch.cast_items.push_back(TileItem{k, int16_t(a), int16_t(b)});
+          ch.prep_items.push_back(TileItem{k, int16_t(a), int16_t(b)});
       const int64_t nr = d.rp / tile, nc = d.cp / tile;
       for (int64_t i = 0; i < nr; ++i)
         for (int64_t j = i; j < nr; ++j) {
@@ -335,7 +338,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
   for (auto* plan : {&pl.ns_full, &pl.ns_block})
     for (NsChunk& ch : *plan)
       for (const NsDev& d : ch.ns)
-        if (d.rp / 128 > 32767 || d.cp / 64 > 32767 || d.nparts > 32767) {
+        if (d.rp / 128 > 32767 || d.cp / 64 > 32767) {
           err = "matrix too large for the tile index range"; return MUON_E_SHAPE;
         }
   // 5. tables
@@ -351,8 +354,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
   for (auto* plan : {&pl.ns_full, &pl.ns_block})
     for (NsChunk& ch : *plan) {
       ch.off_ns = bump.take(ch.ns.size() * sizeof(NsDev));
-      ch.off_mom = bump.take(ch.mom_items.size() * sizeof(TileItem));
-      ch.off_cast = bump.take(ch.cast_items.size() * sizeof(TileItem));
+      ch.off_prep = bump.take(ch.prep_items.size() * sizeof(TileItem));
       for (auto& op : ch.gemm)
         for (auto& gl : op) gl.off = bump.take(gl.items.size() * sizeof(GemmItem));
       ws = std::max(ws, ch.ws_bytes);
@@ -503,16 +505,12 @@ muon_status run_ns(muon_ctx* ctx, std::vector<NsChunk>& chunks) {
   const int prec = c.ns_precision == MUON_NS_BF16 ? 0 : 1;
   for (NsChunk& ch : chunks) {
     NsDev* ns = reinterpret_cast<NsDev*>(ctx->base + ch.off_ns);
-    const TileItem* mom = reinterpret_cast<const TileItem*>(ctx->base + ch.off_mom);
-    const TileItem* cast = reinterpret_cast<const TileItem*>(ctx->base + ch.off_cast);
-    MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_MOMENTUM,
-                             launch_ns_momentum(ctx->stream, mats, ns, mom,
-                                                int64_t(ch.mom_items.size()), c.beta)));
+    const TileItem* prep = reinterpret_cast<const TileItem*>(ctx->base + ch.off_prep);
+    MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_PREP,
+                             launch_ns_prep(ctx->stream, mats, ns, prep,
+                                            int64_t(ch.prep_items.size()), prec, c.beta)));
     MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_SCALE,
                              launch_ns_scale(ctx->stream, ns, int32_t(ch.ns.size()), c.ns_eps)));
-    MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_CAST,
-                             launch_ns_cast(ctx->stream, mats, ns, cast,
-                                            int64_t(ch.cast_items.size()), prec)));
     for (int it = 0; it < c.ns_iters; ++it) {
       const int last = it == c.ns_iters - 1;
       for (int op = 0; op < 3; ++op)
@@ -643,8 +641,7 @@ muon_status muon_init(muon_ctx** out, const muon_config* cfg, const muon_tensor*
   for (auto* plan : {&pl.ns_full, &pl.ns_block})
     for (NsChunk& ch : *plan) {
       if ((e = upload(ctx, ch.off_ns, ch.ns)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
-      if ((e = upload(ctx, ch.off_mom, ch.mom_items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
-      if ((e = upload(ctx, ch.off_cast, ch.cast_items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
+      if ((e = upload(ctx, ch.off_prep, ch.prep_items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
       for (auto& op : ch.gemm)
         for (auto& gl : op)
           if ((e = upload(ctx, gl.off, gl.items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");

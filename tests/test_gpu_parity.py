@@ -142,6 +142,16 @@ def test_single_256x512_ns5_against_svd_polar_band():
     sess.close()
 
 
+@pytest.mark.parametrize("std", [1e-6, 1.0, 1e3])
+def test_refresh_gradient_scale_sweep(std):
+    """The polar factor of M equals that of kappa * M: a refresh step must
+    match the oracle whatever the gradient's magnitude (the Frobenius
+    pre-scale must reach every entry of X X^T and of X_1)."""
+    shapes = [(256, 512), (512, 256), (300, 700), (1200, 1030)]
+    for prec in (0, 1):
+        run_direction_parity(shapes, 1, grad_dtype="f32", grad_std=std, seed=3, ns_precision=prec)
+
+
 # ------------------------------------------------------------------ ragged sets
 RAGGED = [(300, 700), (700, 300), (128, 128), (1, 64), (64, 1), (260, 260), (33, 2050),
           (2050, 33), (1200, 1030)]
