@@ -45,7 +45,64 @@ def ns5_class_flops(shapes, iters=5):
         g += r * r * c
         p += float(r) ** 3
         x += 2.0 * r * r * c
-    return {"ns_gram": iters * g, "ns_poly": iters * p, "ns_product": iters * x}
+    return {"ns_gram": iters * g, "ns_poly": iters * p, "ns_product": (iters - 1) * x,
+            "ns_product_last": x}
+
+
+def ns5_class_bytes(shapes, es=2):
+    """Minimal HBM bytes per launch-set of each NS5 product class: every
+    operand read once and every result written once (es = workspace bytes
+    per value).  Gram: read X, write A; poly: read A, write B; product: read
+    B and X, write X; last product: read B, X and W (fp32), write W."""
+    g = p = x = xl = 0.0
+    for m, n in shapes:
+        r, c = min(m, n), max(m, n)
+        g += es * (r * c + r * r)
+        p += es * 2 * r * r
+        x += es * (r * r + 2 * r * c)
+        xl += es * (r * r + r * c) + 8 * r * c
+    return {"ns_gram": g, "ns_poly": p, "ns_product": x, "ns_product_last": xl}
+
+
+def cnt_per(name: str, cfg) -> int:
+    """Launch-sets of a class per refresh step (one per Newton-Schulz round;
+    the last product runs once)."""
+    if name == "ns_product_last":
+        return 1
+    return cfg.ns_iters - 1 if name == "ns_product" else cfg.ns_iters
+
+
+def source_digest() -> str:
+    """sha256 over the library's sources (csrc/), so that counter figures
+    taken on other sources are not reported."""
+    import hashlib
+    d = os.path.join(HERE, "matrix_aware_optimizer_periodic_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from its committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy), or
+    None when there is none or it was taken on other sources."""
+    path = os.path.join(HERE, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def rownorm_class_bytes(shapes, gbytes):
@@ -111,7 +168,7 @@ def main() -> int:
     ap.add_argument("--K", type=int, default=None, help="refresh period (default 3)")
     ap.add_argument("--no-adamw", action="store_true", help="leave out the bias vectors")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=1)
+    ap.add_argument("--cpu-sample-blocks", type=int, default=2)
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--ws-gib", type=float, default=None, help="NS5 workspace cap (GiB)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -171,9 +228,8 @@ def main() -> int:
     for t in range(args.warmup):
         sess.step(t)
     torch.cuda.synchronize()
-    if not args.no_kernel_timing:
-        mm.muon_timing_read(sess.ctx)          # discard warm-up records
-        mm.muon_timing_enable(sess.ctx, True)
+
+    # Timed region: exactly `steps` optimizer steps, events on the step stream.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -185,8 +241,20 @@ def main() -> int:
     wall = time.perf_counter() - t_wall
     step_ms = [starts[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
     total_ms = sum(step_ms)
-    kt = mm.muon_timing_read(sess.ctx) if not args.no_kernel_timing else {}
-    mm.muon_timing_enable(sess.ctx, False)
+
+    # Per-kernel durations: the same steps again (same branch sequence, K | t0),
+    # with the library's own HIP event pairs around every launch on its stream.
+    kt = {}
+    if not args.no_kernel_timing:
+        t1 = args.warmup + args.steps
+        t1 += (-(t1 - args.warmup)) % K
+        mm.muon_timing_read(sess.ctx)          # clear
+        mm.muon_timing_enable(sess.ctx, True)
+        for k in range(args.steps):
+            sess.step(t1 + k)
+        torch.cuda.synchronize()
+        kt = mm.muon_timing_read(sess.ctx)
+        mm.muon_timing_enable(sess.ctx, False)
 
     branches = [sess.branch(args.warmup + k) for k in range(args.steps)]
     by_branch = {}
@@ -217,6 +285,7 @@ def main() -> int:
     kernels = {}
     if kt:
         nb = rownorm_class_bytes(shapes, gbytes)
+        nsb = ns5_class_bytes(shapes, 2 if args.ns_precision == "bf16" else 4)
         n_rn = branches.count(mm.MUON_BRANCH_ROWNORM)
         for name, (ms, cnt) in kt.items():
             if cnt == 0:
@@ -225,7 +294,8 @@ def main() -> int:
             if name in fl and n_refresh:
                 per = fl[name] * n_refresh / cnt
                 rec.update(bound="mfma", work_per_launch=per, achieved=per / (ms / cnt * 1e-3) / 1e12,
-                           unit="TFLOP/s", peak=peak_mm / 1e12)
+                           unit="TFLOP/s", peak=peak_mm / 1e12,
+                           min_bytes_per_launch=nsb[name] * n_refresh * cnt_per(name, cfg) / cnt)
             elif name in nb and n_rn:
                 per = nb[name] * n_rn / cnt
                 rec.update(bound="hbm", work_per_launch=per, achieved=per / (ms / cnt * 1e-3) / 1e9,
@@ -239,8 +309,10 @@ def main() -> int:
             r = kernels[dom]
             roofline = {"kernel": dom, "bound": r["bound"], "achieved": r["achieved"],
                         "peak": r["peak"], "unit": r["unit"], "frac": r["frac"],
-                        "traffic": None, "avg_launch_ms": r["avg_ms"],
+                        "traffic": measured_traffic(dom, wl.name), "avg_launch_ms": r["avg_ms"],
                         "work_per_launch": r["work_per_launch"]}
+            if "min_bytes_per_launch" in r:
+                roofline["min_bytes_per_launch"] = r["min_bytes_per_launch"]
 
     cpu = None
     if not args.no_cpu_baseline:

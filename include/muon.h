@@ -191,9 +191,10 @@ typedef enum muon_kernel_class {
   MUON_K_NS_SCALE = 4,       /* refresh: 1 / (||M||_F + eps)                 */
   MUON_K_NS_GRAM = 5,        /* refresh: A = X X^T                           */
   MUON_K_NS_POLY = 6,        /* refresh: B = b A + c A A                     */
-  MUON_K_NS_PRODUCT = 7,     /* refresh: X = a X + B X (last: W update)      */
-  MUON_K_ADAMW = 8,          /* AdamW on the non-matrix tensors              */
-  MUON_K_COUNT = 9
+  MUON_K_NS_PRODUCT = 7,     /* refresh: X = a X + B X, rounds 1 .. n-1      */
+  MUON_K_NS_PRODUCT_LAST = 8,/* refresh: last round, fused W update          */
+  MUON_K_ADAMW = 9,          /* AdamW on the non-matrix tensors              */
+  MUON_K_COUNT = 10
 } muon_kernel_class;
 
 /* While enabled (enable != 0), muon_step records a HIP event before and

@@ -518,7 +518,7 @@ muon_status run_ns(muon_ctx* ctx, std::vector<NsChunk>& chunks) {
           const GemmList& gl = ch.gemm[op][t];
           if (gl.items.empty()) continue;
           const GemmItem* items = reinterpret_cast<const GemmItem*>(ctx->base + gl.off);
-          MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_GRAM + op,
+          MUON_HIP(ctx, MUON_TIMED(ctx, op == 2 && last ? MUON_K_NS_PRODUCT_LAST : MUON_K_NS_GRAM + op,
                                    launch_ns_gemm(ctx->stream, mats, ns, items,
                                                   int64_t(gl.items.size()), op, t ? 256 : 128,
                                                   prec, it, last, c.ns_a, c.ns_b, c.ns_c,

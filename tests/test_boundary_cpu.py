@@ -39,6 +39,15 @@ def test_exports_every_declared_function():
         assert hasattr(lib, name), name
 
 
+def test_kernel_classes_follow_the_header_enum():
+    text = open(HEADER).read()
+    pairs = re.findall(r"^\s*MUON_K_(\w+)\s*=\s*(\d+)", text, re.M)
+    enum = {name.lower(): int(v) for name, v in pairs}
+    count = enum.pop("count")
+    assert count == len(m.KERNEL_CLASSES)
+    assert [n for n, _ in sorted(enum.items(), key=lambda kv: kv[1])] == list(m.KERNEL_CLASSES)
+
+
 def test_defaults_match_the_pages_and_the_oracle():
     c = m.muon_config_default()
     o = oracle.OracleConfig()
