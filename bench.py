@@ -268,11 +268,22 @@ def main() -> int:
     peak_mm = PEAK_BF16 if args.ns_precision == "bf16" else PEAK_F32
     fl = ns5_class_flops(shapes, cfg.ns_iters)
     f_refresh = sum(fl.values())
+    # MuonBP block steps orthogonalise bp_blocks column blocks of each matrix
+    blk_shapes = [(m, n // cfg.bp_blocks) for m, n in shapes for _ in range(cfg.bp_blocks)] \
+        if cfg.bp_blocks else []
+    flb = ns5_class_flops(blk_shapes, cfg.ns_iters) if blk_shapes else {}
+    f_block = sum(flb.values())
+    n_block = branches.count(mm.MUON_BRANCH_BLOCK_NS5)
     ns5 = None
     if "ns5" in branch_ms:
         tf = f_refresh / (branch_ms["ns5"] * 1e-3)
         ns5 = {"step_ms": branch_ms["ns5"], "tflops": tf / 1e12, "frac": tf / peak_mm,
                "flops_alg": f_refresh}
+    block_ns5 = None
+    if "block_ns5" in branch_ms:
+        tf = f_block / (branch_ms["block_ns5"] * 1e-3)
+        block_ns5 = {"step_ms": branch_ms["block_ns5"], "tflops": tf / 1e12, "frac": tf / peak_mm,
+                     "flops_alg": f_block}
     elems = sum(m * n for m, n in shapes)
     gbytes = 2 if gdt == torch.bfloat16 else 4
     rown = None
@@ -291,11 +302,12 @@ def main() -> int:
             if cnt == 0:
                 continue
             rec = {"total_ms": ms, "launches": cnt, "avg_ms": ms / cnt}
-            if name in fl and n_refresh:
-                per = fl[name] * n_refresh / cnt
+            if name in fl and (n_refresh or n_block):
+                per = (fl[name] * n_refresh + flb.get(name, 0.0) * n_block) / cnt
                 rec.update(bound="mfma", work_per_launch=per, achieved=per / (ms / cnt * 1e-3) / 1e12,
-                           unit="TFLOP/s", peak=peak_mm / 1e12,
-                           min_bytes_per_launch=nsb[name] * n_refresh * cnt_per(name, cfg) / cnt)
+                           unit="TFLOP/s", peak=peak_mm / 1e12)
+                if not n_block:
+                    rec["min_bytes_per_launch"] = nsb[name] * n_refresh * cnt_per(name, cfg) / cnt
             elif name in nb and n_rn:
                 per = nb[name] * n_rn / cnt
                 rec.update(bound="hbm", work_per_launch=per, achieved=per / (ms / cnt * 1e-3) / 1e9,
@@ -347,6 +359,7 @@ def main() -> int:
         },
         "branch_ms": branch_ms,
         "ns5": ns5,
+        "block_ns5": block_ns5,
         "rownorm": rown,
         "roofline": roofline,
         "kernels": kernels,
