@@ -48,6 +48,13 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    # A kernel whose launch stub the host pass dropped still links (the
+    # library is shared) and only fails when loaded: refuse it here.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "muon" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError(f"library has undefined symbols of its own: {missing[:4]}")
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}", file=sys.stderr)

@@ -373,17 +373,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // Stages past the end are issued as a reload of the last stage: the loop
   // body then has no branches (exact wait counts), and the buffer such a
   // reload lands in is one no wave reads any more.
+  // The per-lane byte offsets do not change along k: they stay in VGPRs, and
+  // the stage's k offset goes in the scalar offset.  The LDS destination
+  // (M0) is wave-uniform scalar arithmetic too, so a DMA costs two scalar
+  // instructions and the load.
+  // (A local array of these offsets captured by the lambda below makes the
+  // host compilation pass drop this kernel's launch stub, silently.)
+  const int swid = __builtin_amdgcn_readfirstlane(wid);
+  auto issue_one = [&](int kt, int q) {
+    const int kb = min(kt, nk - 1) * 64;
+    LOCAL unsigned char* base =
+        (LOCAL unsigned char*)(smem + (kt % NSTAGE) * STAGE + swid * 1024);
+    const unsigned voff = q < DMA / 2 ? offP + unsigned(q) * rstride
+                                      : offQ + unsigned(q - DMA / 2) * rstride;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(q < DMA / 2 ? rP : rQ,
+                                             (LOCAL void*)(base + q * NW * 1024), 16, voff, kb,
+                                             0, 0);
+  };
   auto issue = [&](int kt) {
-    const unsigned kb = unsigned(min(kt, nk - 1)) * 64u;
-    LOCAL unsigned char* base = (LOCAL unsigned char*)(smem + (kt % NSTAGE) * STAGE + wid * 1024);
 #pragma unroll
-    for (int q = 0; q < DMA; ++q) {
-      const bool isP = q < DMA / 2;
-      const unsigned off = (isP ? offP + unsigned(q) * rstride
-                                : offQ + unsigned(q - DMA / 2) * rstride) + kb;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isP ? rP : rQ, (LOCAL void*)(base + q * NW * 1024),
-                                               16, off, 0, 0, 0);
-    }
+    for (int q = 0; q < DMA; ++q) issue_one(kt, q);
   };
 
   f32x16_t acc[FM][FN];
@@ -403,30 +412,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
 #pragma unroll
     for (int f = 0; f < FN; ++f) fb[f] = sQ[(wn * WN + f * 32 + frow) * 4 + ch];
   };
-  auto mma = [&](const u32x4_t* fa, const u32x4_t* fb) {
-#pragma unroll
-    for (int x = 0; x < FM; ++x)
-#pragma unroll
-      for (int y = 0; y < FN; ++y) {
-        if constexpr (sizeof(T) == 2) {
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, fa[x]), __builtin_bit_cast(bf16x8_t, fb[y]), acc[x][y],
-              0, 0, 0);
-        } else {
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                __uint_as_float(fa[x][s]), __uint_as_float(fb[y][s]), acc[x][y], 0, 0, 0);
-        }
-      }
+  // One fragment (index < FM: P, else Q) of k-group g.
+  auto frag_one = [&](const u32x4_t* sP, const u32x4_t* sQ, int g, int f, u32x4_t* fa,
+                      u32x4_t* fb) {
+    const int ch = (2 * g + fhalf) ^ fsw;
+    if (f < FM) fa[f] = sP[(wm * WM + f * 32 + frow) * 4 + ch];
+    else fb[f - FM] = sQ[(wn * WN + (f - FM) * 32 + frow) * 4 + ch];
   };
-  // Software pipeline.  At the top of iteration kt the registers hold the
-  // fragments of both k-groups of stage kt.  The MFMAs of group 0 run; then
-  // this wave waits for its own DMA of stage kt+1 and all waves meet at a
-  // barrier (so every part of stage kt+1 is in LDS, and every wave has
-  // finished reading stage kt-1, whose buffer the DMA of stage kt+3 takes);
-  // the fragments of stage kt+1 are read while the MFMAs of group 1 of
-  // stage kt run.  LDS latency thus always hides behind a group of MFMAs.
+  // MFMAs of one k-group over the flattened fragment pairs [lo, hi).
+  auto mma = [&](const u32x4_t* fa, const u32x4_t* fb, int lo, int hi) {
+#pragma unroll
+    for (int xy = 0; xy < FM * FN; ++xy) {
+      if (xy < lo || xy >= hi) continue;
+      const int x = xy / FN, y = xy % FN;
+      if constexpr (sizeof(T) == 2) {
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, fa[x]), __builtin_bit_cast(bf16x8_t, fb[y]), acc[x][y],
+            0, 0, 0);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+              __uint_as_float(fa[x][s]), __uint_as_float(fb[y][s]), acc[x][y], 0, 0, 0);
+      }
+    }
+  };
+  // Software pipeline, two k-groups (g0, g1) per stage.  With one wave per
+  // SIMD the matrix core idles whenever its wave issues anything but MFMAs,
+  // so the other instructions are spread between MFMAs in fixed slots (one
+  // MFMA pair, then at most one DMA and one LDS fragment read; sched_barrier
+  // keeps each slot together), and the workgroup barrier sits behind MFMAs
+  // already issued.
+  //
+  // Iteration kt starts with the g0 fragments of stage kt in registers.
+  //   part 1: MFMAs of g0, with the LDS reads of the g1 fragments of stage kt
+  //           (landed and visible since the barrier of iteration kt - 1)
+  //           between them; then the first PRE MFMAs of g1.
+  //   wait for this wave's DMA of stage kt + 1, then the barrier: every part
+  //   of stage kt + 1 is in LDS, and every wave has finished reading stage
+  //   kt - 1, whose buffer the DMA of stage kt + 3 refills.
+  //   part 2: the rest of g1's MFMAs, with the DMA of stage kt + 3 and the
+  //           LDS reads of the g0 fragments of stage kt + 1 between them.
   // The barrier is a bare s_barrier: __syncthreads() would add a release
   // fence that waits for every DMA in flight, i.e. for the stages
   // prefetched ahead.
@@ -438,6 +464,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  constexpr int NXY = FM * FN;                       // fragment pairs per k-group
+  constexpr int PRE = NXY >= 16 ? 2 : 1;             // g1 pairs issued before the barrier
+  constexpr int NRD = FM + FN;                       // LDS reads per k-group
+  static_assert(NRD <= NXY && DMA + NRD <= 2 * (NXY - PRE) + 2, "slots for every read");
   u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
   {
     wait_vmcnt<2 * DMA>();          // stage 0 is in; stages 1, 2 may be in flight
@@ -445,25 +475,53 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const u32x4_t *sP, *sQ;
     stage_ptrs(0, sP, sQ);
     frag(sP, sQ, 0, a0, b0);
-    frag(sP, sQ, 1, a1, b1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
   // Every iteration issues exactly DMA loads, so after the waits below the
   // only DMA in flight is that of stage kt + 2.  The fragment reads of stage
   // nk (past the end) read a reloaded buffer and are never used.
   for (int kt = 0; kt < nk; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
+    {
+      const u32x4_t *sP, *sQ;
+      stage_ptrs(kt, sP, sQ);
+#pragma unroll
+      for (int i = 0; i < NXY; ++i) {
+        mma(a0, b0, i, i + 1);
+        if (i < NRD) frag_one(sP, sQ, 1, i, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < PRE; ++i) {
+        mma(a1, b1, i, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     wait_vmcnt<DMA>();
     bar();
-    issue(kt + NSTAGE - 1);
-    const u32x4_t *sP, *sQ;
-    stage_ptrs(kt + 1, sP, sQ);
-    frag(sP, sQ, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
+    {
+      const u32x4_t *sP, *sQ;
+      stage_ptrs(kt + 1, sP, sQ);
+      // DMA and reads alternate over the slots: slot i carries DMA i/2 on
+      // even i and read i/2 on odd i while both remain, then whatever is left.
+      int nd = 0, nr = 0;
+#pragma unroll
+      for (int i = PRE; i < NXY; ++i) {
+        mma(a1, b1, i, i + 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (nd < DMA && (nr >= NRD || nd <= nr)) { issue_one(kt + NSTAGE - 1, nd); ++nd; }
+          else if (nr < NRD) { frag_one(sP, sQ, 0, nr, a0, b0); ++nr; }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (; nd < DMA; ++nd) issue_one(kt + NSTAGE - 1, nd);
+#pragma unroll
+      for (; nr < NRD; ++nr) frag_one(sP, sQ, 0, nr, a0, b0);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    frag(sP, sQ, 1, a1, b1);
   }
   wait_vmcnt<0>();
   __syncthreads();
