@@ -35,6 +35,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short bf16x4_raw_t __attribute__((ext_vector_type(4)));
 
 // Pointers into global memory.  The workspace pointers come out of launch
 // tables, so the compiler cannot tell they are global; without the address
@@ -78,7 +79,8 @@ __device__ __forceinline__ float load_g(const void* g, int gdt, int64_t idx) {
 // Refresh-step preparation, one 64 x 64 tile of the padded stored block per
 // workgroup: M <- beta M + G for the tile's valid elements, the tile's sum of
 // squares (one partial per tile), and the new M, unscaled, cast to the
-// workspace type in both layouts (Xr and Xc[0]); padding is written as 0.
+// workspace type: X = M (wide) or M^T (tall, through an LDS transpose) into
+// x[0], and for fp32 also X^T into xt[0]; padding is written as 0.
 // The pre-normalisation factor s = 1 / (||M||_F + eps) is applied by the
 // first Newton-Schulz round instead (A = s^2 X X^T, X_1 = s (a X + B X)),
 // which saves a second pass over M.
@@ -92,9 +94,10 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
   const NsDev d = ns[it.id];
   const MatDev mt = mats[d.mat];
   const int64_t p0 = int64_t(it.ti) * kPrepTile, q0 = int64_t(it.tj) * kPrepTile;
-  T* dst = static_cast<T*>(d.tall ? d.xc[0] : d.xr);     // stored orientation
+  // stored orientation and its transpose; bf16 keeps only X itself
+  T* dst = static_cast<T*>(d.tall ? d.xt[0] : d.x[0]);
   const int64_t ldd = d.tall ? d.rp : d.cp;
-  T* dstt = static_cast<T*>(d.tall ? d.xr : d.xc[0]);    // transposed
+  T* dstt = static_cast<T*>(d.tall ? d.x[0] : d.xt[0]);
   const int64_t ldt = d.tall ? d.cp : d.rp;
   const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
   const bool vec = ((d.ld | d.col0) & 3) == 0 && q0 + kPrepTile <= d.cols;
@@ -136,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
       ss += v[u] * v[u];
       tile[lr][tc + u] = v[u];
     }
+    if (dst == nullptr) continue;
     T* o = dst + p * ldd + q0 + tc;
     if constexpr (sizeof(T) == 2) {
       const uint32_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
@@ -147,6 +151,7 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
   }
   const float tot = block_sum(ss, red);   // contains the barrier the transpose needs
   if (threadIdx.x == 0) d.part[int64_t(it.ti) * (d.tall ? d.rp : d.cp) / kPrepTile + it.tj] = tot;
+  if (dstt == nullptr) return;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int lq = tr + 16 * pass;
@@ -302,6 +307,29 @@ __device__ __forceinline__ void wait_vmcnt() {
   else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 }
 
+// 16 bytes per lane from a raw buffer straight into LDS (lane l lands at
+// lds_addr + 16 l).  Issued as inline asm so that the compiler does not
+// model these LDS writes: it cannot tell them apart from the transposed LDS
+// reads, and would otherwise drain every DMA in flight before each such
+// read.  The GEMM pipeline orders them itself (explicit vmcnt waits and
+// barriers).
+__device__ __forceinline__ void dma16(u32x4_t rsrc, unsigned lds_addr, unsigned voff,
+                                      unsigned soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "m0");
+}
+
+// Raw buffer resource: base, stride 0, byte size (reads past it return 0).
+__device__ __forceinline__ u32x4_t buffer_rsrc(const void* p, int64_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4_t{unsigned(a), unsigned(a >> 32) & 0xffffu, unsigned(nbytes), 0x00020000u};
+}
+
 template <typename T, int BM, int WGM, int WGN, int OP>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
@@ -310,6 +338,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // OP kGemmProductLast is the product of the last round (updates W).
   constexpr bool PROD = OP == kGemmProduct || OP == kGemmProductLast;
   constexpr bool last = OP == kGemmProductLast;
+  // bf16 product: the X operand is staged from row-major X (32 rows of k by
+  // the tile's BM columns) and read with transposed LDS loads.
+  constexpr bool QT = PROD && sizeof(T) == 2;
   constexpr int NW = WGM * WGN;
   constexpr int NT = 64 * NW;                // threads
   constexpr int WM = BM / WGM, WN = BM / WGN;
@@ -333,19 +364,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   const GemmItem it = items[blockIdx.x];
   const NsDev d = ns[it.ns];
   const int cur = iter & 1;
+  // X of this round: bf16 alternates x[0] / x[1]; fp32 keeps it in x[0].
+  const T* xcur = static_cast<const T*>(sizeof(T) == 2 && cur ? d.x[1] : d.x[0]);
   const T* P;
   const T* Q;
-  int64_t ld, K;
+  int64_t ld, ldq, K;
   if constexpr (OP == kGemmGram) {
-    P = Q = static_cast<const T*>(d.xr); ld = d.cp; K = d.cp;
+    P = Q = xcur; ld = ldq = d.cp; K = d.cp;
   } else if constexpr (OP == kGemmPoly) {
-    P = Q = static_cast<const T*>(d.a); ld = d.rp; K = d.rp;
+    P = Q = static_cast<const T*>(d.a); ld = ldq = d.rp; K = d.rp;
   } else {
     static_assert(PROD, "unknown op");
     P = static_cast<const T*>(d.b);
-    Q = static_cast<const T*>(cur ? d.xc[1] : d.xc[0]);
     ld = d.rp;
     K = d.rp;
+    if constexpr (QT) {
+      Q = xcur; ldq = d.cp;                  // X itself, rows k
+    } else {
+      Q = static_cast<const T*>(cur ? d.xt[1] : d.xt[0]); ldq = d.rp;   // X^T, rows j
+    }
   }
   const int64_t i0 = int64_t(it.ti) * BM, j0 = int64_t(it.tj) * BM;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -359,17 +396,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // buffer loads into LDS: unlike the FLAT form they count only against the
   // vector-memory counter, so waiting for LDS fragment reads does not also
   // wait for the prefetch in flight.  Offsets past a buffer's end read 0.
+  //
+  // QT: the Q part of a stage is X rows k .. k + 31, columns j0 .. j0 + BM - 1
+  // (2 BM bytes per row, CPRQ 16-byte chunks); DMA block b holds rows
+  // RPB b .. RPB b + RPB - 1 and lane l brings row RPB b + l / CPRQ, logical
+  // chunk (l % CPRQ) ^ ((row & 3) << 2), which lands at physical chunk
+  // l % CPRQ.  The XOR puts the four rows a transposed read touches in four
+  // distinct 64-byte bank groups.
   const int drow = 16 * wid + (lane >> 2);
   const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const int64_t prow = d.rp;   // P is Xr, A or B: rp rows
-  const int64_t qrow = PROD ? d.cp : d.rp;
-  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(P), 0, int(prow * ld * int64_t(sizeof(T))), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(Q), 0, int(qrow * ld * int64_t(sizeof(T))), 0x00020000);
+  constexpr int CPRQ = BM / 8, RPB = 64 / CPRQ;
+  static_assert(!QT || (RPB * NW) % 4 == 0, "row phase of a lane fixed across its blocks");
+  const int qtrow = RPB * wid + lane / CPRQ;
+  const int qtchunk = (lane % CPRQ) ^ ((qtrow & 3) << 2);
+  const int64_t prow = d.rp;   // P is X, A or B: rp rows
+  const int64_t qrow = QT ? d.rp : (PROD ? d.cp : d.rp);
+  const u32x4_t rP = buffer_rsrc(P, prow * ld * int64_t(sizeof(T)));
+  const u32x4_t rQ = buffer_rsrc(Q, qrow * ldq * int64_t(sizeof(T)));
   const unsigned offP = unsigned((i0 + drow) * ld * int64_t(sizeof(T))) + unsigned(dchunk * 16);
-  const unsigned offQ = unsigned((j0 + drow) * ld * int64_t(sizeof(T))) + unsigned(dchunk * 16);
   const unsigned rstride = unsigned(int64_t(16 * NW) * ld * int64_t(sizeof(T)));
+  const unsigned offQ =
+      QT ? unsigned((int64_t(qtrow) * ldq + j0 + 8 * qtchunk) * int64_t(sizeof(T)))
+         : unsigned((j0 + drow) * ldq * int64_t(sizeof(T))) + unsigned(dchunk * 16);
+  const unsigned rstrideQ = unsigned(int64_t(QT ? RPB * NW : 16 * NW) * ldq * int64_t(sizeof(T)));
+  // bytes per stage along k: 64 (k contiguous) or KT rows of X (QT)
+  const int64_t kstepQ = QT ? int64_t(KT) * ldq * int64_t(sizeof(T)) : 64;
   // Stages past the end are issued as a reload of the last stage: the loop
   // body then has no branches (exact wait counts), and the buffer such a
   // reload lands in is one no wave reads any more.
@@ -381,14 +432,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // host compilation pass drop this kernel's launch stub, silently.)
   const int swid = __builtin_amdgcn_readfirstlane(wid);
   auto issue_one = [&](int kt, int q) {
-    const int kb = min(kt, nk - 1) * 64;
+    const int kc = min(kt, nk - 1);
+    const int kb = q < DMA / 2 ? kc * 64 : int(kc * kstepQ);
     LOCAL unsigned char* base =
         (LOCAL unsigned char*)(smem + (kt % NSTAGE) * STAGE + swid * 1024);
     const unsigned voff = q < DMA / 2 ? offP + unsigned(q) * rstride
-                                      : offQ + unsigned(q - DMA / 2) * rstride;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(q < DMA / 2 ? rP : rQ,
-                                             (LOCAL void*)(base + q * NW * 1024), 16, voff, kb,
-                                             0, 0);
+                                      : offQ + unsigned(q - DMA / 2) * rstrideQ;
+    dma16(q < DMA / 2 ? rP : rQ, unsigned(uintptr_t(base + q * NW * 1024)), voff, unsigned(kb));
   };
   auto issue = [&](int kt) {
 #pragma unroll
@@ -404,20 +454,55 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   for (int s0 = 0; s0 < NSTAGE - 1; ++s0) issue(s0);
 
   const int frow = lane & 31, fsw = (lane >> 2) & 3, fhalf = lane >> 5;
+  // QT fragments.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of
+  // a group receives element i & 3 of the 8 bytes addressed by lane
+  // 4 e + (i >> 2), for e = 0..3.  Lane s of a group therefore addresses row
+  // k0 + (s >> 2), columns c0 + 4 (s & 3) .. + 3, and lane i receives column
+  // c0 + i of rows k0 .. k0 + 3: four consecutive k of one column of X, as
+  // the MFMA operand wants them.  Two such reads (h = 0, 1) give a lane its
+  // 8 k values: k = 16 g + 8 (l >> 5) + 4 h + e, column (l & 31) of the
+  // fragment.
+  const int trow = 8 * (lane >> 5) + ((lane & 15) >> 2);          // + 16 g + 4 h
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);         // + fragment column
+  const int tsw = (trow & 3) << 2;
+  auto qtr = [&](const u32x4_t* sQ, int g, int f, int h, u32x4_t& out) {
+    const int row = 16 * g + 4 * h + trow;
+    const int col = wn * WN + f * 32 + tcol;
+    const int byte = row * (2 * BM) + (((col >> 3) ^ tsw) << 4) + ((col & 7) << 1);
+    const LOCAL bf16x4_raw_t* p =
+        (const LOCAL bf16x4_raw_t*)((const LOCAL unsigned char*)sQ + byte);
+    const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                          (LOCAL bf16x4_raw_t*)p));
+    out[2 * h] = w[0];
+    out[2 * h + 1] = w[1];
+  };
   // Fragments of k-group g (16 k values) of one stage.
   auto frag = [&](const u32x4_t* sP, const u32x4_t* sQ, int g, u32x4_t* fa, u32x4_t* fb) {
     const int ch = (2 * g + fhalf) ^ fsw;
 #pragma unroll
     for (int f = 0; f < FM; ++f) fa[f] = sP[(wm * WM + f * 32 + frow) * 4 + ch];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) fb[f] = sQ[(wn * WN + f * 32 + frow) * 4 + ch];
+    for (int f = 0; f < FN; ++f) {
+      if constexpr (QT) {
+        qtr(sQ, g, f, 0, fb[f]);
+        qtr(sQ, g, f, 1, fb[f]);
+      } else {
+        fb[f] = sQ[(wn * WN + f * 32 + frow) * 4 + ch];
+      }
+    }
   };
-  // One fragment (index < FM: P, else Q) of k-group g.
+  // One LDS read of k-group g: index f < FM is P fragment f; after that Q
+  // fragments, one read each, or (QT) two transposed reads each.
   auto frag_one = [&](const u32x4_t* sP, const u32x4_t* sQ, int g, int f, u32x4_t* fa,
                       u32x4_t* fb) {
     const int ch = (2 * g + fhalf) ^ fsw;
-    if (f < FM) fa[f] = sP[(wm * WM + f * 32 + frow) * 4 + ch];
-    else fb[f - FM] = sQ[(wn * WN + (f - FM) * 32 + frow) * 4 + ch];
+    if (f < FM) {
+      fa[f] = sP[(wm * WM + f * 32 + frow) * 4 + ch];
+    } else if constexpr (QT) {
+      qtr(sQ, g, (f - FM) >> 1, (f - FM) & 1, fb[(f - FM) >> 1]);
+    } else {
+      fb[f - FM] = sQ[(wn * WN + (f - FM) * 32 + frow) * 4 + ch];
+    }
   };
   // MFMAs of one k-group over the flattened fragment pairs [lo, hi).
   auto mma = [&](const u32x4_t* fa, const u32x4_t* fb, int lo, int hi) {
@@ -466,8 +551,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   };
   constexpr int NXY = FM * FN;                       // fragment pairs per k-group
   constexpr int PRE = NXY >= 16 ? 2 : 1;             // g1 pairs issued before the barrier
-  constexpr int NRD = FM + FN;                       // LDS reads per k-group
-  static_assert(NRD <= NXY && DMA + NRD <= 2 * (NXY - PRE) + 2, "slots for every read");
+  constexpr int NRD = FM + (QT ? 2 : 1) * FN;        // LDS reads per k-group
   u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
   {
     wait_vmcnt<2 * DMA>();          // stage 0 is in; stages 1, 2 may be in flight
@@ -492,6 +576,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
+      for (int i = NXY; i < NRD; ++i) frag_one(sP, sQ, 1, i, a1, b1);
+#pragma unroll
       for (int i = 0; i < PRE; ++i) {
         mma(a1, b1, i, i + 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -503,16 +589,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     {
       const u32x4_t *sP, *sQ;
       stage_ptrs(kt + 1, sP, sQ);
-      // DMA and reads alternate over the slots: slot i carries DMA i/2 on
-      // even i and read i/2 on odd i while both remain, then whatever is left.
+      // Each slot carries up to two of: the LDS reads first, then the DMA.
+      // Reads go first because the compiler cannot tell a transposed LDS read
+      // from the DMA's LDS writes apart, and before a read placed after a DMA
+      // it would wait for every DMA in flight.
       int nd = 0, nr = 0;
 #pragma unroll
       for (int i = PRE; i < NXY; ++i) {
         mma(a1, b1, i, i + 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          if (nd < DMA && (nr >= NRD || nd <= nr)) { issue_one(kt + NSTAGE - 1, nd); ++nd; }
-          else if (nr < NRD) { frag_one(sP, sQ, 0, nr, a0, b0); ++nr; }
+          if (nr < NRD) { frag_one(sP, sQ, 0, nr, a0, b0); ++nr; }
+          else if (nd < DMA) { issue_one(kt + NSTAGE - 1, nd); ++nd; }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -535,12 +623,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // when bit 2 of sw(r) is set.
   float* stage = reinterpret_cast<float*>(smem);
   const bool diag_tile = it.ti == it.tj;
-  T* xr = static_cast<T*>(d.xr);
-  T* xcn = static_cast<T*>(cur ? d.xc[0] : d.xc[1]);
+  const T* xin = xcur;                                              // X of this round
+  T* xout = static_cast<T*>(QT ? (cur ? d.x[0] : d.x[1]) : d.x[0]);  // next X (fp32: in place)
+  T* xtn = static_cast<T*>(cur ? d.xt[0] : d.xt[1]);                // fp32: next X^T
   float* w = mats[d.mat].w;
   const float wkeep = 1.0f - d.lr * wd;
   bool mirror;
-  if constexpr (PROD) mirror = !last || d.tall;
+  if constexpr (PROD) mirror = QT ? (last && d.tall) : (!last || d.tall);
   else mirror = !diag_tile;
   auto sw = [](int r) { return ((r >> 4) & 7) << 2; };
   // Round 0 works on the unscaled M: A = s^2 (M M^T), X_1 = s (a M + B M).
@@ -578,7 +667,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         const int r = idx / CPR, ch = idx % CPR;
         const int64_t i = ib0 + r, j = j0 + ch * 8;
         if constexpr (OP == kGemmPoly) ra[q].load(static_cast<const T*>(d.a) + i * d.rp + j);
-        else ra[q].load(xr + i * d.cp + j);
+        else ra[q].load(xin + i * d.cp + j);
         if (aux_is_w) {
           const int nv = (i < d.r) ? int(max<int64_t>(0, min<int64_t>(8, d.c - j))) : 0;
           const int64_t e0 = i * d.ld + d.col0 + j;
@@ -665,8 +754,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
             ra[q].unpack(xv);
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
-            store8(xr + i * d.cp + j, v);
-            writeback = true;
+            store8(xout + i * d.cp + j, v);
+            writeback = !QT;                // fp32 also writes X^T from the stage
           } else if (!d.tall) {
             float xv[8], wv[8];
             ra[q].unpack(xv);
@@ -723,7 +812,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           store8(static_cast<T*>(d.b) + j * d.rp + i, v);
         } else {
           if constexpr (!last) {
-            store8(xcn + j * d.rp + i, v);
+            store8(xtn + j * d.rp + i, v);
           } else if (j < d.c) {
             const int nv = int(max<int64_t>(0, min<int64_t>(8, d.r - i)));
             if (nv > 0) w_update8(w, j * d.ld + d.col0 + i, nv, v, d.lr, wkeep);

@@ -176,8 +176,8 @@ size_t problem_ws_bytes(const Problem& p, int tile, size_t es, int64_t* rp_out, 
   const int32_t nparts = static_cast<int32_t>((rp / kPrepTile) * (cp / kPrepTile));
   *rp_out = rp; *cp_out = cp; *nparts_out = nparts;
   size_t b = 0;
-  b += align_up(size_t(rp) * cp * es, kAlign);          // xr
-  b += 2 * align_up(size_t(cp) * rp * es, kAlign);      // xc[0], xc[1]
+  b += 2 * align_up(size_t(rp) * cp * es, kAlign);      // bf16: x[0], x[1]; fp32: x[0], xt[0]
+  if (es == 4) b += align_up(size_t(cp) * rp * es, kAlign);   // fp32: xt[1]
   b += 2 * align_up(size_t(rp) * rp * es, kAlign);      // a, b
   b += align_up(size_t(nparts) * 4, kAlign);            // partials
   b += kAlign;                                          // scale
@@ -189,9 +189,6 @@ int tile_for(int64_t r) { return r >= 1024 ? 256 : 128; }
 
 constexpr int64_t kSuperRows = 8, kSuperCols = 4;
 
-// Tall RowNorm matrices run phase 1 and phase 2 group by group, each group's
-// new momentum (written by phase 1, re-read by phase 2) small enough to stay
-// in the 256 MB Infinity Cache between the two launches.
 std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_config& cfg) {
   const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
   std::vector<NsChunk> chunks;
@@ -384,9 +381,17 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
       for (size_t k = 0; k < ch.ns.size(); ++k) {
         NsDev& d = ch.ns[k];
         size_t o = pl.ws_base + ch.ws_off[k];
-        d.xr = at(o); o += align_up(size_t(d.rp) * d.cp * es, kAlign);
-        d.xc[0] = at(o); o += align_up(size_t(d.cp) * d.rp * es, kAlign);
-        d.xc[1] = at(o); o += align_up(size_t(d.cp) * d.rp * es, kAlign);
+        const size_t xb = align_up(size_t(d.rp) * d.cp * es, kAlign);
+        if (es == 2) {
+          d.x[0] = at(o); o += xb;
+          d.x[1] = at(o); o += xb;
+          d.xt[0] = d.xt[1] = nullptr;
+        } else {
+          d.x[0] = at(o); o += xb;
+          d.x[1] = nullptr;
+          d.xt[0] = at(o); o += xb;
+          d.xt[1] = at(o); o += xb;
+        }
         d.a = at(o); o += align_up(size_t(d.rp) * d.rp * es, kAlign);
         d.b = at(o); o += align_up(size_t(d.rp) * d.rp * es, kAlign);
         d.part = static_cast<float*>(at(o)); o += align_up(size_t(d.nparts) * 4, kAlign);
