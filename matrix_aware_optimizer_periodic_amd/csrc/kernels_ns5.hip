@@ -553,6 +553,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   constexpr int PRE = NXY >= 16 ? 2 : 1;             // g1 pairs issued before the barrier
   constexpr int NRD = FM + (QT ? 2 : 1) * FN;        // LDS reads per k-group
   u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
+  // QT: remainder lo_i of the diagonal a + B_ii for row (lane & 31) of each
+  // fragment row fa, and the stage that holds those rows of X for fa = 0.
+  float dlo[FM];
+  const int kf0 = int(it.ti) * (BM / 32) + (swid / WGN) * FM;   // scalar: a uniform branch
+  if constexpr (QT) {
+#pragma unroll
+    for (int fa = 0; fa < FM; ++fa) dlo[fa] = d.bdiag[i0 + wm * WM + fa * 32 + (lane & 31)];
+  }
   {
     wait_vmcnt<2 * DMA>();          // stage 0 is in; stages 1, 2 may be in flight
     bar();
@@ -582,6 +590,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         mma(a1, b1, i, i + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (QT) {
+        // Stage kt holds rows 32 kt .. 32 kt + 31 of X, i.e. (for one fa)
+        // X_i of this wave's output rows: add lo_i X_i with MFMAs whose P
+        // operand is diag(lo) over those 32 rows (B itself carries bf16(a +
+        // B_ii) on its diagonal).
+#pragma unroll
+        for (int fa = 0; fa < FM; ++fa) {
+          if (kt == kf0 + fa) {
+            const uint32_t bits = f32_to_bf16(dlo[fa]);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const int e = (lane & 31) - 16 * g - 8 * (lane >> 5);
+              u32x4_t f = {0u, 0u, 0u, 0u};
+#pragma unroll
+              for (int w2 = 0; w2 < 4; ++w2)
+                f[w2] = (e >= 0 && (e >> 1) == w2) ? bits << (16 * (e & 1)) : 0u;
+#pragma unroll
+              for (int y = 0; y < FN; ++y)
+                acc[fa][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8_t, f),
+                    __builtin_bit_cast(bf16x8_t, g ? b1[y] : b0[y]), acc[fa][y], 0, 0, 0);
+            }
+          }
+        }
+      }
     }
     wait_vmcnt<DMA>();
     bar();
@@ -589,18 +622,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     {
       const u32x4_t *sP, *sQ;
       stage_ptrs(kt + 1, sP, sQ);
-      // Each slot carries up to two of: the LDS reads first, then the DMA.
-      // Reads go first because the compiler cannot tell a transposed LDS read
-      // from the DMA's LDS writes apart, and before a read placed after a DMA
-      // it would wait for every DMA in flight.
+      // Each slot carries up to two of the DMAs and LDS reads, alternating
+      // while both remain.
       int nd = 0, nr = 0;
 #pragma unroll
       for (int i = PRE; i < NXY; ++i) {
         mma(a1, b1, i, i + 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          if (nr < NRD) { frag_one(sP, sQ, 0, nr, a0, b0); ++nr; }
-          else if (nd < DMA) { issue_one(kt + NSTAGE - 1, nd); ++nd; }
+          if (nd < DMA && (nr >= NRD || nd <= nr)) { issue_one(kt + NSTAGE - 1, nd); ++nd; }
+          else if (nr < NRD) { frag_one(sP, sQ, 0, nr, a0, b0); ++nr; }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -644,8 +675,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // product, plus W for the last product of a wide matrix).  They are issued in
   // batches of PB chunks, the first batch before the accumulators are
   // parked, so their latency overlaps the staging and its barrier.
-  const bool need_aux = OP == kGemmPoly || PROD;
   const bool aux_is_w = last && !d.tall;     // also the W values to update
+  const bool need_aux = OP == kGemmPoly || (PROD && (!QT || aux_is_w));
   // Batch size: as many chunks in flight as registers allow without spills
   // (8 packed bf16 chunks; 4 for fp32 and for the last product, which also
   // carries W).
@@ -667,7 +698,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         const int r = idx / CPR, ch = idx % CPR;
         const int64_t i = ib0 + r, j = j0 + ch * 8;
         if constexpr (OP == kGemmPoly) ra[q].load(static_cast<const T*>(d.a) + i * d.rp + j);
-        else ra[q].load(xin + i * d.cp + j);
+        else if constexpr (!QT) ra[q].load(xin + i * d.cp + j);
         if (aux_is_w) {
           const int nv = (i < d.r) ? int(max<int64_t>(0, min<int64_t>(8, d.c - j))) : 0;
           const int64_t e0 = i * d.ld + d.col0 + j;
@@ -731,6 +762,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         } else if constexpr (OP == kGemmPoly) {
           float av[8];
           ra[q].unpack(av);
+          float dval = 0.f;          // stored diagonal (bf16: a + B_ii; fp32: 0)
           if (has_diag) {
             float acc_ii = 0.f, a_ii = 0.f;
 #pragma unroll
@@ -740,25 +772,36 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
             }
             const float ad = d.adiag[i];
             const float aa = acc_ii + ad * ad - a_ii * a_ii;
-            d.bdiag[i] = fmaf(cb, ad, cc * aa);
+            const float bii = fmaf(cb, ad, cc * aa);
+            if constexpr (sizeof(T) == 2) {
+              // stored B_ii = bf16(a + B_ii); the remainder goes to the product
+              // as an extra diagonal MFMA operand
+              const float dsum = ca + bii;
+              dval = dsum;
+              d.bdiag[i] = dsum - bf16_to_f32(f32_to_bf16(dsum));
+            } else {
+              d.bdiag[i] = bii;
+            }
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            v[u] = (has_diag && u == du) ? 0.f : fmaf(cc, v[u], cb * av[u]);
+            v[u] = (has_diag && u == du) ? dval : fmaf(cc, v[u], cb * av[u]);
           store8(static_cast<T*>(d.b) + i * d.rp + j, v);
           writeback = true;
         } else {
-          const float mlt = ca + d.bdiag[i];
-          if constexpr (!last) {
-            float xv[8];
+          // fp32: add (a + B_ii) X_i here; bf16: the MFMAs already did
+          float mlt = 0.f, xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if constexpr (!QT) {
+            mlt = ca + d.bdiag[i];
             ra[q].unpack(xv);
+          }
+          if constexpr (!last) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
             store8(xout + i * d.cp + j, v);
             writeback = !QT;                // fp32 also writes X^T from the stage
           } else if (!d.tall) {
-            float xv[8], wv[8];
-            ra[q].unpack(xv);
+            float wv[8];
             rw[q].unpack(wv);
 #pragma unroll
             for (int u = 0; u < 8; ++u)
@@ -775,8 +818,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
                 if (u < nv) gw[u] = v[u];
             }
           } else {
-            float xv[8];
-            ra[q].unpack(xv);
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
             writeback = true;

@@ -59,7 +59,8 @@ struct NsDev {
   float* part;       // Frobenius partial sums, one per prep tile (nparts)
   float* scale;      // s = 1 / (||M||_F + eps), one float
   float* adiag;      // rp: diagonal of A kept in fp32
-  float* bdiag;      // rp: diagonal of B kept in fp32 (stored B has 0 there)
+  float* bdiag;      // rp, fp32: B_ii (stored B has 0 there); bf16: stored B
+                     // holds bf16(a + B_ii) and this the rounding remainder
   int32_t nparts;
   float lr;          // learning rate applied by the final product
 };

@@ -147,11 +147,20 @@ int row_chunk_class(int64_t cols) {
 // Reorder a natural-order work list so the hardware's round-robin dispatch
 // (workgroup i -> XCD i mod 8) gives each XCD one contiguous segment of it:
 // neighbouring tiles, which share operand panels, then meet in the same L2.
-template <typename T>
-void xcd_interleave(std::vector<T>& v) {
+//
+// With a cost per item, each XCD's segment is also ordered longest first
+// (stable, so a matrix's tiles stay together): the launch then ends on short
+// tiles instead of leaving most CUs idle behind a few long ones.
+template <typename T, typename Cost>
+void xcd_interleave(std::vector<T>& v, Cost cost) {
   const int64_t n = static_cast<int64_t>(v.size());
   if (n < 16) return;
   const int64_t q = n / 8, rem = n % 8;
+  for (int64_t x = 0; x < 8; ++x) {
+    const int64_t b = x * q + std::min<int64_t>(x, rem), e = b + q + (x < rem ? 1 : 0);
+    std::stable_sort(v.begin() + b, v.begin() + e,
+                     [&](const T& l, const T& r) { return cost(l) > cost(r); });
+  }
   std::vector<T> out;
   out.reserve(v.size());
   for (int64_t local = 0; local <= q; ++local)
@@ -242,8 +251,12 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
             for (int64_t j = jb; j < std::min(nc, jb + kSuperCols); ++j)
               ch.gemm[kGemmProduct][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
     }
-    for (auto& op : ch.gemm)
-      for (auto& gl : op) xcd_interleave(gl.items);
+    // A tile costs its K: cp for the Gram, rp for the polynomial and product.
+    for (int op = 0; op < 3; ++op)
+      for (auto& gl : ch.gemm[op])
+        xcd_interleave(gl.items, [&](const GemmItem& g) {
+          return op == kGemmGram ? ch.ns[g.ns].cp : ch.ns[g.ns].rp;
+        });
   }
   return chunks;
 }
