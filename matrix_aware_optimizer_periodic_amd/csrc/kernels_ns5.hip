@@ -262,19 +262,21 @@ template <> struct Raw8<float> {
 };
 
 // GEMM tile C[i0.., j0..] = sum_k P[i][k] Q[j][k] on MFMA, BM x BM per
-// workgroup of WGM x WGN waves, each wave (BM/WGM) x (BM/WGN) built from
-// 32 x 32 MFMA blocks.  256-tiles run 8 waves (two per SIMD, so one wave's
-// MFMAs cover the other's waits); 128-tiles run 4.
+// workgroup of 2 x 2 waves (one per SIMD), each wave (BM/2) x (BM/2) built
+// from 32 x 32 MFMA blocks; a 256-tile wave holds its 128 x 128 fp32
+// accumulators in the 256 AGPRs.
 //
 // Operand staging.  The k loop runs over stages of 64 bytes of k (32 bf16 or
-// 16 fp32) for all 2 BM rows of P and Q, NSTAGE stages deep in LDS.  Global
-// data goes straight to LDS (global_load_lds_dwordx4: each lane's 16 bytes
-// land at the wave's LDS base + 16 * lane), issued NSTAGE - 1 stages ahead of
-// its use, so no registers hold operands in flight.  A 64-byte LDS row holds
-// four 16-byte chunks; chunk c of row r sits at position c ^ ((r >> 2) & 3).
-// gfx950 serves a 128-bit LDS read in groups of 16 lanes over 64 banks, and
-// with this placement the 16 consecutive rows such a group reads at one
-// logical chunk fall on 16 distinct bank groups.
+// 16 fp32) for all 2 BM rows of P and Q, NSTAGE stages deep in LDS (as many
+// 4 for 256-tiles, 5 for 128-tiles).  Global data goes straight to LDS (MUBUF
+// buffer_load ... lds: each lane's 16 bytes land at the wave's LDS base +
+// 16 * lane), issued NSTAGE - 1 stages ahead of its use, so no registers
+// hold operands in flight.  A 64-byte LDS row holds four 16-byte chunks;
+// chunk c of row r sits at position c ^ ((r >> 2) & 3).  gfx950 serves a
+// 128-bit LDS read in groups of 16 lanes over 64 banks, and with this
+// placement the 16 consecutive rows such a group reads at one logical chunk
+// fall on 16 distinct bank groups.  The bf16 product stages its X operand
+// as rows of X instead (see QT below) and reads it transposed.
 //
 // MFMA operand layout used (both 32 x 32 variants): lane l supplies row
 // (l & 31) of P and of Q; its k values are the 16-byte chunk 2g + (l >> 5) of
@@ -286,25 +288,22 @@ template <> struct Raw8<float> {
 // Epilogue, per half of the tile's rows: the owning waves park their
 // accumulators in LDS, then all threads write the outputs in 16-byte chunks,
 // first along rows (C, or W of a wide matrix), then along columns (the
-// mirrored half of a symmetric A or B, X^T, or W of a tall matrix).
+// mirrored half of a symmetric A or B, X^T in fp32, or W of a tall matrix).
 //
-// Rounding.  The diagonals of A and B stay in fp32 (adiag, bdiag): B's
-// diagonal is applied as (a + B_ii) X_i in fp32 and stored as 0 in the bf16
-// operand, and the A_ii^2 term of (A A)_ii and the b A_ii term use the fp32
-// A_ii.  This is the same arithmetic, rounded later: it avoids the
-// cancellation between a and B_ii that bf16 storage of B_ii would amplify
-// when the short side r is small.
+// Rounding.  The diagonal of A stays in fp32 (adiag), and the A_ii^2 term of
+// (A A)_ii and the b A_ii term use it.  B's diagonal a + B_ii (the product
+// applies aI + B) is kept to about 2^-18: fp32 stores 0 in B and applies
+// (a + B_ii) X_i in fp32 in the epilogue; bf16 stores bf16(a + B_ii) in B and
+// adds the remainder with extra diagonal MFMAs.  This is the same arithmetic,
+// rounded later: it avoids the cancellation between a and B_ii that plain
+// bf16 storage of B_ii would amplify when the short side r is small.
 #define LOCAL __attribute__((address_space(3)))
 
 // s_waitcnt vmcnt(N) for the DMA counts the GEMM pipeline uses.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N == 0 || N == 2 || N == 4 || N == 8 || N == 16, "unsupported wait count");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // 16 bytes per lane from a raw buffer straight into LDS (lane l lands at
@@ -346,7 +345,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   constexpr int WM = BM / WGM, WN = BM / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int ROWS = 2 * BM;               // P rows then Q rows
-  constexpr int NSTAGE = 4;
+  // Stages in the LDS ring: 4 for 256-tiles (of 160 KB), 5 for 128-tiles
+  // (80 KB, two workgroups per CU); deeper rings measured no faster.
+  constexpr int NSTAGE = BM >= 256 ? 4 : 5;
   constexpr int STAGE = ROWS * 64;           // bytes per stage
   constexpr int BLOCKS = ROWS / 16;          // 16-row (1 KB) DMA blocks per stage
   constexpr int DMA = BLOCKS / NW;           // DMA instructions per wave per stage
@@ -535,8 +536,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   //           between them; then the first PRE MFMAs of g1.
   //   wait for this wave's DMA of stage kt + 1, then the barrier: every part
   //   of stage kt + 1 is in LDS, and every wave has finished reading stage
-  //   kt - 1, whose buffer the DMA of stage kt + 3 refills.
-  //   part 2: the rest of g1's MFMAs, with the DMA of stage kt + 3 and the
+  //   kt - 1, whose buffer the DMA of stage kt + NSTAGE - 1 refills.
+  //   part 2: the rest of g1's MFMAs, with the DMA of stage kt + NSTAGE - 1 and the
   //           LDS reads of the g0 fragments of stage kt + 1 between them.
   // The barrier is a bare s_barrier: __syncthreads() would add a release
   // fence that waits for every DMA in flight, i.e. for the stages
@@ -562,7 +563,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     for (int fa = 0; fa < FM; ++fa) dlo[fa] = d.bdiag[i0 + wm * WM + fa * 32 + (lane & 31)];
   }
   {
-    wait_vmcnt<2 * DMA>();          // stage 0 is in; stages 1, 2 may be in flight
+    wait_vmcnt<(NSTAGE - 2) * DMA>();   // stage 0 is in; stages 1 .. NSTAGE-2 may be in flight
     bar();
     const u32x4_t *sP, *sQ;
     stage_ptrs(0, sP, sQ);
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
   // Every iteration issues exactly DMA loads, so after the waits below the
-  // only DMA in flight is that of stage kt + 2.  The fragment reads of stage
+  // DMAs in flight are those of stages kt + 2 .. kt + NSTAGE - 2.  The fragment reads of stage
   // nk (past the end) read a reloaded buffer and are never used.
   for (int kt = 0; kt < nk; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
@@ -616,7 +617,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         }
       }
     }
-    wait_vmcnt<DMA>();
+    wait_vmcnt<(NSTAGE - 3) * DMA>();
     bar();
     __builtin_amdgcn_sched_barrier(0);
     {
