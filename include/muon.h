@@ -194,7 +194,8 @@ typedef enum muon_kernel_class {
   MUON_K_NS_PRODUCT = 7,     /* refresh: X = a X + B X, rounds 1 .. n-1      */
   MUON_K_NS_PRODUCT_LAST = 8,/* refresh: last round, fused W update          */
   MUON_K_ADAMW = 9,          /* AdamW on the non-matrix tensors              */
-  MUON_K_COUNT = 10
+  MUON_K_ROWNORM_COEF = 10,  /* RowNorm step, tall: column coefficients      */
+  MUON_K_COUNT = 11
 } muon_kernel_class;
 
 /* While enabled (enable != 0), muon_step records a HIP event before and

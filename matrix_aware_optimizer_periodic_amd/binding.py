@@ -27,7 +27,7 @@ EXPORTED = ("muon_config_default", "muon_state_bytes", "muon_init", "muon_step",
 
 # muon_kernel_class, in enum order
 KERNEL_CLASSES = ("rownorm_rows", "rownorm_cols1", "rownorm_cols2", "ns_prep", "ns_scale",
-                  "ns_gram", "ns_poly", "ns_product", "ns_product_last", "adamw")
+                  "ns_gram", "ns_poly", "ns_product", "ns_product_last", "adamw", "rownorm_coef")
 
 
 class MuonTensor(ctypes.Structure):

@@ -142,8 +142,9 @@ __global__ __launch_bounds__(kThreads) void rownorm_rows_kernel(
 // Tall matrices, slices = columns.  A tile is kColTileRows x kColTileCols;
 // thread (rg = tid / 64, ct = tid % 64) owns 4 columns and rows rg, rg+4, ...
 // Phase 1 writes the new momentum and one partial column sum of squares per
-// (row tile, column); phase 2 adds the partials of all row tiles in order,
-// then scales and updates W.
+// (row tile, column); rownorm_coef_kernel adds each column's partials over
+// the row tiles in order and leaves lr * gamma / max(||column||, eps) in the
+// first partial row; phase 2 scales and updates W.
 // Phase 2 visits the tiles in reverse order, so the momentum phase 1 wrote
 // last (most likely still in the Infinity Cache) is read first.
 template <int PHASE>
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void rownorm_cols_kernel(
     if (vec) {
       const int64_t col = c0 + ct * 4;
       if (col < n) {
+#pragma unroll 8
         for (int64_t r = r0 + rg; r < r1; r += 4) {
           const int64_t e = r * n + col;
           const float4 g = load_g4(d.g, d.gdt, e);
@@ -204,19 +206,18 @@ __global__ __launch_bounds__(kThreads) void rownorm_cols_kernel(
       }
     }
   } else {
+    (void)nchunk;
     float coef[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t col = c0 + lc[v];
-      float s = 0.f;
-      if (col < n)
-        for (int64_t k = 0; k < nchunk; ++k) s += d.part[k * n + col];
-      coef[v] = sc.lr * sc.gamma / fmaxf(sqrtf(s), sc.eps_row);
+      coef[v] = col < n ? d.part[col] : 0.f;
     }
     const float wkeep = 1.0f - sc.lr * sc.wd;
     if (vec) {
       const int64_t col = c0 + ct * 4;
       if (col < n) {
+#pragma unroll 8
         for (int64_t r = r0 + rg; r < r1; r += 4) {
           const int64_t e = r * n + col;
           const float4 mm = *reinterpret_cast<const float4*>(d.mom + e);
@@ -241,7 +242,32 @@ __global__ __launch_bounds__(kThreads) void rownorm_cols_kernel(
   }
 }
 
+// One workgroup per column strip (kColTileCols columns) of a tall matrix:
+// each column's partial sums of squares over the row tiles, added in row
+// order, become its update coefficient, stored in the first partial row.
+__global__ __launch_bounds__(kThreads) void rownorm_coef_kernel(
+    const MatDev* __restrict__ mats, const TileItem* __restrict__ strips, StepScalars sc) {
+  const TileItem it = strips[blockIdx.x];
+  const MatDev d = mats[it.id];
+  const int64_t n = d.cols;
+  const int64_t nchunk = (d.rows + kColTileRows - 1) / kColTileRows;
+  const int64_t col = int64_t(it.tj) * kColTileCols + threadIdx.x;
+  if (col >= n) return;
+  float s = 0.f;
+  for (int64_t k = 0; k < nchunk; ++k) s += d.part[k * n + col];
+  d.part[col] = sc.lr * sc.gamma / fmaxf(sqrtf(s), sc.eps_row);
+}
+
 }  // namespace
+
+hipError_t launch_rownorm_coef(hipStream_t s, const MatDev* mats, const TileItem* strips,
+                               int64_t nstrips, StepScalars sc) {
+  if (nstrips <= 0) return hipSuccess;
+  static_assert(kColTileCols == kThreads, "one thread per strip column");
+  rownorm_coef_kernel<<<dim3(static_cast<unsigned>(nstrips)), dim3(kThreads), 0, s>>>(mats, strips,
+                                                                                     sc);
+  return hipGetLastError();
+}
 
 hipError_t launch_rownorm_rows(hipStream_t s, const MatDev* mats, const int32_t* mat_ids,
                                const int64_t* row_prefix, int32_t nmat, int64_t total_rows,

@@ -101,6 +101,8 @@ hipError_t launch_rownorm_rows(hipStream_t s, const MatDev* mats, const int32_t*
                                int max_chunks, StepScalars sc);
 // Column-normalised (tall) matrices, phase 1 (momentum + column partials) or
 // phase 2 (norms + weight update), one workgroup per tile.
+hipError_t launch_rownorm_coef(hipStream_t s, const MatDev* mats, const TileItem* strips,
+                               int64_t nstrips, StepScalars sc);
 hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem* tiles,
                                int64_t ntiles, int phase, StepScalars sc);
 // Refresh prep: momentum, Frobenius partials, unscaled X0 in both layouts.

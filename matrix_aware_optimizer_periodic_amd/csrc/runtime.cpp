@@ -64,9 +64,10 @@ struct Plan {
   std::vector<size_t> mom_off, part_off, m_off, v_off;
   std::vector<RowGroup> row_groups;
   std::vector<TileItem> col_tiles;
+  std::vector<TileItem> col_strips;   // (matrix, 0, column strip) of the tall matrices
   std::vector<AdamChunk> adam_chunks;
   std::vector<NsChunk> ns_full, ns_block;
-  size_t off_mats = 0, off_adams = 0, off_col_tiles = 0, off_adam_chunks = 0;
+  size_t off_mats = 0, off_adams = 0, off_col_tiles = 0, off_col_strips = 0, off_adam_chunks = 0;
   size_t ws_base = 0, ws_bytes = 0;
   size_t zero_end = 0;                    // bytes [0, zero_end) are zeroed at init
   size_t total = 0;
@@ -306,6 +307,8 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
       for (int64_t a = 0; a < nchunk; ++a)
         for (int64_t b = 0; b < ceil_div(t.cols, kColTileCols); ++b)
           pl.col_tiles.push_back(TileItem{mi, int16_t(a), int16_t(b)});
+      for (int64_t b = 0; b < ceil_div(t.cols, kColTileCols); ++b)
+        pl.col_strips.push_back(TileItem{mi, 0, int16_t(b)});
     } else {
       const int cls = row_chunk_class(t.cols);
       RowGroup& g = groups[std::find(classes, classes + 7, cls) - classes];
@@ -355,6 +358,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
   pl.off_mats = bump.take(pl.mats.size() * sizeof(MatDev));
   pl.off_adams = bump.take(pl.adams.size() * sizeof(AdamDev));
   pl.off_col_tiles = bump.take(pl.col_tiles.size() * sizeof(TileItem));
+  pl.off_col_strips = bump.take(pl.col_strips.size() * sizeof(TileItem));
   pl.off_adam_chunks = bump.take(pl.adam_chunks.size() * sizeof(AdamChunk));
   for (RowGroup& g : pl.row_groups) {
     g.off_ids = bump.take(g.ids.size() * 4);
@@ -649,7 +653,8 @@ muon_status muon_init(muon_ctx** out, const muon_config* cfg, const muon_tensor*
   }
   const hipError_t ups[] = {
       upload(ctx, pl.off_mats, pl.mats), upload(ctx, pl.off_adams, pl.adams),
-      upload(ctx, pl.off_col_tiles, pl.col_tiles), upload(ctx, pl.off_adam_chunks, pl.adam_chunks)};
+      upload(ctx, pl.off_col_tiles, pl.col_tiles), upload(ctx, pl.off_col_strips, pl.col_strips),
+      upload(ctx, pl.off_adam_chunks, pl.adam_chunks)};
   for (hipError_t u : ups)
     if (u != hipSuccess) return fail(u, "hipMemcpyAsync(tables)");
   for (RowGroup& g : pl.row_groups) {
@@ -740,7 +745,14 @@ muon_status muon_step(muon_ctx* ctx, const muon_tensor* params, const muon_tenso
         if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_rows"); }
       }
       const TileItem* tiles = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_tiles);
+      const TileItem* strips = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_strips);
       for (int phase = 1; phase <= 2 && !pl.col_tiles.empty(); ++phase) {
+        if (phase == 2) {
+          const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_COEF,
+                                          launch_rownorm_coef(ctx->stream, mats, strips,
+                                                              int64_t(pl.col_strips.size()), sc));
+          if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_coef"); }
+        }
         const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_COLS1 + phase - 1,
                                         launch_rownorm_cols(ctx->stream, mats, tiles,
                                                             int64_t(pl.col_tiles.size()), phase, sc));
