@@ -245,16 +245,26 @@ def main() -> int:
     # Per-kernel durations: the same steps again (same branch sequence, K | t0),
     # with the library's own HIP event pairs around every launch on its stream.
     kt = {}
+    kt_branch = {}
     if not args.no_kernel_timing:
         t1 = args.warmup + args.steps
         t1 += (-(t1 - args.warmup)) % K
         mm.muon_timing_read(sess.ctx)          # clear
         mm.muon_timing_enable(sess.ctx, True)
+        kt_branch = {}
         for k in range(args.steps):
             sess.step(t1 + k)
-        torch.cuda.synchronize()
-        kt = mm.muon_timing_read(sess.ctx)
+            torch.cuda.synchronize()
+            rec = mm.muon_timing_read(sess.ctx)
+            acc = kt_branch.setdefault(sess.branch(t1 + k), {})
+            for name, (ms, cnt) in rec.items():
+                a = acc.get(name, (0.0, 0))
+                acc[name] = (a[0] + ms, a[1] + cnt)
         mm.muon_timing_enable(sess.ctx, False)
+        for acc in kt_branch.values():
+            for name, (ms, cnt) in acc.items():
+                a = kt.get(name, (0.0, 0))
+                kt[name] = (a[0] + ms, a[1] + cnt)
 
     branches = [sess.branch(args.warmup + k) for k in range(args.steps)]
     by_branch = {}
@@ -363,6 +373,9 @@ def main() -> int:
         "rownorm": rown,
         "roofline": roofline,
         "kernels": kernels,
+        "kernel_ms_by_branch": {names[b]: {k: round(v[0] / max(1, branches.count(b)), 4)
+                                           for k, v in acc.items() if v[1]}
+                                for b, acc in kt_branch.items()},
         "cpu_baseline": cpu,
         "wall_s": wall,
         "device": torch.cuda.get_device_name(dev),
