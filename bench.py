@@ -121,11 +121,23 @@ def rownorm_class_bytes(shapes, gbytes):
 def cpu_baseline(wl, cfg_over, sample_blocks=1):
     """The fp64 oracle as it stands, one K-cycle on a sample of blocks."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     ocfg = oracle.OracleConfig(**cfg_over)
     per_block = len(workloads.dit_block_shapes(wl.d)) if wl.d else len(wl.shapes)
     shapes = [(m, n) for _, m, n in wl.shapes[:per_block * sample_blocks]]
@@ -141,6 +153,7 @@ def cpu_baseline(wl, cfg_over, sample_blocks=1):
     scale = (wl.blocks / sample_blocks) if wl.blocks else 1.0
     steps_per_s = K / (dt * scale)
     return {"value": steps_per_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu_model, "blas": blas, "numpy": np.__version__,
             "sample": f"{len(shapes)} matrices ({sample_blocks} of {wl.blocks or 1} blocks), one "
                       f"{K}-step cycle, {dt:.1f} s, scaled x{scale:g} to the whole set",
             "sample_seconds": dt}

@@ -465,3 +465,59 @@ def test_dit_full_set_sampled(name):
         sess.close()
         del params, grads
         torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ graph capture
+def test_step_replays_from_hip_graphs():
+    """muon_step only enqueues kernels (no allocation, no synchronisation), so
+    each branch of a K-cycle can be captured once in a HIP graph and replayed.
+    Replays, with eager gradient copies and synchronisations between them,
+    must give bitwise the same weights and momentum as eager steps.  Only
+    matrices here: an AdamW tensor's bias correction depends on t, which a
+    captured launch would freeze."""
+    m = _lib()
+    shapes = [(256, 640), (640, 256), (300, 700)]
+    K = 3
+    W0 = [torch.from_numpy(workloads.host_weight0(4, i, s)).cuda() for i, s in enumerate(shapes)]
+
+    def make():
+        W = [w.clone() for w in W0]
+        G = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+        return W, G
+
+    stream = torch.cuda.Stream()
+    We, Ge = make()
+    Wg, Gg = make()
+    with torch.cuda.stream(stream):
+        eager = m.MuonSession(We, Ge, stream=stream, K=K)
+        graphed = m.MuonSession(Wg, Gg, stream=stream, K=K)
+    graphs = []
+    try:
+        grads = lambda t: [torch.from_numpy(workloads.host_grad(6, t, i, s, 1e-3, "bf16")).to(
+            torch.bfloat16).cuda() for i, s in enumerate(shapes)]
+        # capture one step per branch position of the cycle, t = 0 .. K-1
+        torch.cuda.synchronize()
+        for t in range(K):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                graphed.step(t)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for t in range(3 * K):
+            gt = grads(t)
+            for dst_e, dst_g, src in zip(Ge, Gg, gt):
+                dst_e.copy_(src)
+                dst_g.copy_(src)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                eager.step(t)
+            graphs[t % K].replay()
+            torch.cuda.synchronize()
+            for i in range(len(shapes)):
+                assert torch.equal(We[i], Wg[i]), f"t={t} matrix {i}: W differs"
+                assert torch.equal(eager.state_view(i), graphed.state_view(i)), f"t={t} matrix {i}"
+        print(f"{3 * K} graph replays match eager steps bitwise", flush=True)
+    finally:
+        del graphs
+        eager.close()
+        graphed.close()
