@@ -55,12 +55,14 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32: round to
+// nearest even, NaN stays NaN), one value or a packed pair.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
@@ -142,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
     if (dst == nullptr) continue;
     T* o = dst + p * ldd + q0 + tc;
     if constexpr (sizeof(T) == 2) {
-      const uint32_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-      const uint32_t hi = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      const uint32_t lo = pack_bf16x2(v[0], v[1]);
+      const uint32_t hi = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<u32x2_t*>(o) = u32x2_t{lo, hi};
     } else {
       *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
@@ -160,8 +162,8 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
     for (int u = 0; u < 4; ++u) v[u] = tile[tc + u][lq];
     T* o = dstt + (q0 + lq) * ldt + p0 + tc;
     if constexpr (sizeof(T) == 2) {
-      const uint32_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-      const uint32_t hi = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      const uint32_t lo = pack_bf16x2(v[0], v[1]);
+      const uint32_t hi = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<u32x2_t*>(o) = u32x2_t{lo, hi};
     } else {
       *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
@@ -204,7 +206,7 @@ __device__ __forceinline__ void store8(T* p, const float v[8]) {
   if constexpr (sizeof(T) == 2) {
     u32x4_t u;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) u[k] = f32_to_bf16(v[2 * k]) | (f32_to_bf16(v[2 * k + 1]) << 16);
+    for (int k = 0; k < 4; ++k) u[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
     *as_global(reinterpret_cast<u32x4_t*>(p)) = u;
   } else {
     as_global(reinterpret_cast<f32x4_t*>(p))[0] = f32x4_t{v[0], v[1], v[2], v[3]};
@@ -285,7 +287,8 @@ template <> struct Raw8<float> {
 // between the two operands is valid as long as it is the same for both.
 // Accumulator element v of lane l is C[8 (v/4) + 4 (l/32) + (v%4)][l & 31].
 //
-// Epilogue, per half of the tile's rows: the owning waves park their
+// Epilogue, per pass over the tile (whole for 128-tiles, halves for
+// 256-tiles): the owning waves park their
 // accumulators in LDS, then all threads write the outputs in 16-byte chunks,
 // first along rows (C, or W of a wide matrix), then along columns (the
 // mirrored half of a symmetric A or B, X^T in fp32, or W of a tall matrix).
@@ -353,7 +356,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   constexpr int DMA = BLOCKS / NW;           // DMA instructions per wave per stage
   constexpr int KT = 64 / int(sizeof(T));    // k elements per stage
   constexpr int SLD = BM + 4;                // epilogue stage row stride (floats)
-  constexpr int HALF = BM / 2;
+  // Epilogue rows per pass: the whole tile when its fp32 stage fits the LDS
+  // ring (128-tiles), else half of it.
+  constexpr int NPASS = BM >= 256 ? 2 : 1;
+  constexpr int HALF = BM / NPASS;
   constexpr int MAIN_BYTES = NSTAGE * STAGE;
   constexpr int STAGE_BYTES = HALF * SLD * 4;
   constexpr int SMEM = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
@@ -687,7 +693,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   static_assert(NB * PB == DIT, "whole batches");
 
 #pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < NPASS; ++half) {
     const int64_t ib0 = i0 + int64_t(half) * HALF;
     Raw8<T> ra[PB];
     Raw8<float> rw[PB];
