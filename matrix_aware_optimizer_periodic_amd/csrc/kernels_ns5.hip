@@ -214,27 +214,45 @@ __device__ __forceinline__ void store8(T* p, const float v[8]) {
   }
 }
 
-// W[e0 + u] = W[e0 + u] * keep - lr * v[u] for u < nv (the weight update of the
-// last Newton-Schulz round), vectorised when the run is whole and aligned.
-__device__ __forceinline__ void w_update8(float* w, int64_t e0, int nv, const float v[8], float lr,
-                                          float keep) {
-  GLOBAL float* gw = as_global(w) + e0;
-  if (nv == 8 && (e0 & 3) == 0) {
-    f32x4_t a = reinterpret_cast<GLOBAL f32x4_t*>(gw)[0];
-    f32x4_t b = reinterpret_cast<GLOBAL f32x4_t*>(gw)[1];
+// Eight values W[e0 .. e0 + 7] of a weight matrix for the update of the last
+// Newton-Schulz round, W <- W keep - lr v, for the first nv of them:
+// vectorised when the run is whole and aligned, else value by value (zeros
+// past nv).  Loading and storing are separate calls, so that a batch of loads
+// can be in flight while an earlier batch is stored.
+struct W8 {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* w, int64_t e0, int nv) {
+    const GLOBAL float* gw = as_global(w) + e0;
+    if (nv == 8 && (e0 & 3) == 0) {
+      a = reinterpret_cast<const GLOBAL f32x4_t*>(gw)[0];
+      b = reinterpret_cast<const GLOBAL f32x4_t*>(gw)[1];
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      a[k] = fmaf(-lr, v[k], a[k] * keep);
-      b[k] = fmaf(-lr, v[4 + k], b[k] * keep);
+      for (int u = 0; u < 4; ++u) {
+        a[u] = (u < nv) ? gw[u] : 0.f;
+        b[u] = (u + 4 < nv) ? gw[u + 4] : 0.f;
+      }
     }
-    reinterpret_cast<GLOBAL f32x4_t*>(gw)[0] = a;
-    reinterpret_cast<GLOBAL f32x4_t*>(gw)[1] = b;
-  } else {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u < nv) gw[u] = fmaf(-lr, v[u], gw[u] * keep);
   }
-}
+  __device__ __forceinline__ void update_store(float* w, int64_t e0, int nv, const float v[8],
+                                               float lr, float keep) const {
+    float o[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      o[u] = fmaf(-lr, v[u], a[u] * keep);
+      o[4 + u] = fmaf(-lr, v[4 + u], b[u] * keep);
+    }
+    GLOBAL float* gw = as_global(w) + e0;
+    if (nv == 8 && (e0 & 3) == 0) {
+      reinterpret_cast<GLOBAL f32x4_t*>(gw)[0] = f32x4_t{o[0], o[1], o[2], o[3]};
+      reinterpret_cast<GLOBAL f32x4_t*>(gw)[1] = f32x4_t{o[4], o[5], o[6], o[7]};
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < nv) gw[u] = o[u];
+    }
+  }
+};
 
 // Eight workspace values kept as loaded (bf16 stays packed) until used.
 template <typename T> struct Raw8;
@@ -680,49 +698,63 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   static_assert(DIT * NT == HALF * CPR && MIT * NT == BM * CPC, "whole passes");
   // The direct pass needs operand reads per chunk (A for B; X for the
   // product, plus W for the last product of a wide matrix).  They are issued in
-  // batches of PB chunks, the first batch before the accumulators are
-  // parked, so their latency overlaps the staging and its barrier.
+  // batches of PB chunks, double-buffered: batch bt + 1 is in flight while
+  // batch bt is computed and stored, and the first batch is issued before the
+  // accumulators are parked, so its latency overlaps the staging and its
+  // barrier.  The last product of a tall matrix updates W in the mirror pass,
+  // in batches of MB chunks, double-buffered the same way, its first batch
+  // issued before the direct pass.
   const bool aux_is_w = last && !d.tall;     // also the W values to update
   const bool need_aux = OP == kGemmPoly || (PROD && (!QT || aux_is_w));
-  // Batch size: as many chunks in flight as registers allow without spills
-  // (8 packed bf16 chunks; 4 for fp32 and for the last product, which also
-  // carries W).
-  constexpr int PBMAX = (last || sizeof(T) == 4) ? 4 : 8;
+  const bool mirror_w = last && d.tall;
+  // Batch sizes: as many chunks in flight as registers allow without spills
+  // (the two W paths share one double buffer of 4-chunk batches).
+  constexpr int PBMAX = sizeof(T) == 4 ? (last ? 1 : 2) : 4;
   constexpr int PB = DIT < PBMAX ? DIT : PBMAX;
   constexpr int NB = DIT / PB;
   static_assert(NB * PB == DIT, "whole batches");
+  constexpr int MBMAX = sizeof(T) == 4 ? 2 : 4;
+  constexpr int MB = MIT < MBMAX ? MIT : MBMAX;
+  constexpr int MNB = MIT / MB;
+  static_assert(MNB * MB == MIT, "whole mirror batches");
 
 #pragma unroll 1
   for (int half = 0; half < NPASS; ++half) {
     const int64_t ib0 = i0 + int64_t(half) * HALF;
-    Raw8<T> ra[PB];
-    Raw8<float> rw[PB];
-    int rw_nv[PB];
+    Raw8<T> ra[2][PB];
+    W8 wb[2][4];
+    static_assert(PB <= 4 && MB <= 4, "W batches fit the shared buffer");
+    // values of a W row run that exist (wide: row i of X is row i of W)
+    auto wide_nv = [&](int64_t i, int64_t j) {
+      return (i < d.r) ? int(max<int64_t>(0, min<int64_t>(8, d.c - j))) : 0;
+    };
     auto prefetch = [&](int bt) {
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
         const int idx = tid + (bt * PB + q) * NT;
         const int r = idx / CPR, ch = idx % CPR;
         const int64_t i = ib0 + r, j = j0 + ch * 8;
-        if constexpr (OP == kGemmPoly) ra[q].load(static_cast<const T*>(d.a) + i * d.rp + j);
-        else if constexpr (!QT) ra[q].load(xin + i * d.cp + j);
-        if (aux_is_w) {
-          const int nv = (i < d.r) ? int(max<int64_t>(0, min<int64_t>(8, d.c - j))) : 0;
-          const int64_t e0 = i * d.ld + d.col0 + j;
-          rw_nv[q] = nv;
-          if (nv == 8 && (e0 & 3) == 0) {
-            rw[q].load(w + e0);
-          } else {
+        if constexpr (OP == kGemmPoly) ra[bt & 1][q].load(static_cast<const T*>(d.a) + i * d.rp + j);
+        else if constexpr (!QT) ra[bt & 1][q].load(xin + i * d.cp + j);
+        if (aux_is_w) wb[bt & 1][q].load(w, i * d.ld + d.col0 + j, wide_nv(i, j));
+      }
+    };
+    // Mirror chunk: column jj of the tile, rows 8 ch .. 8 ch + 7 of this pass,
+    // i.e. a run of row j of X^T (tall: of W).
+    auto mirror_nv = [&](int64_t i, int64_t j) {
+      return (j < d.c) ? int(max<int64_t>(0, min<int64_t>(8, d.r - i))) : 0;
+    };
+    auto mprefetch = [&](int mb) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              rw[q].a[u] = (u < nv) ? as_global(w)[e0 + u] : 0.f;
-              rw[q].b[u] = (u + 4 < nv) ? as_global(w)[e0 + 4 + u] : 0.f;
-            }
-          }
-        }
+      for (int q = 0; q < MB; ++q) {
+        const int idx = tid + (mb * MB + q) * NT;
+        const int jj = idx / CPC, ch = idx % CPC;
+        const int64_t j = j0 + jj, i = ib0 + ch * 8;
+        wb[mb & 1][q].load(w, j * d.ld + d.col0 + i, mirror_nv(i, j));
       }
     };
     if (need_aux) prefetch(0);
+    if (mirror_w) mprefetch(0);
     if (wm * WM >= half * HALF && wm * WM < (half + 1) * HALF) {
       const int rbase = wm * WM - half * HALF;
 #pragma unroll
@@ -740,7 +772,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     // rows of the tile: C[i][j .. j+7]
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) {
-      if (bt > 0 && need_aux) prefetch(bt);
+      if (bt + 1 < NB && need_aux) prefetch(bt + 1);
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
         const int idx = tid + (bt * PB + q) * NT;
@@ -768,7 +800,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           store8(static_cast<T*>(d.a) + i * d.rp + j, v);
         } else if constexpr (OP == kGemmPoly) {
           float av[8];
-          ra[q].unpack(av);
+          ra[bt & 1][q].unpack(av);
           float dval = 0.f;          // stored diagonal (bf16: a + B_ii; fp32: 0)
           if (has_diag) {
             float acc_ii = 0.f, a_ii = 0.f;
@@ -800,7 +832,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           float mlt = 0.f, xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
           if constexpr (!QT) {
             mlt = ca + d.bdiag[i];
-            ra[q].unpack(xv);
+            ra[bt & 1][q].unpack(xv);
           }
           if constexpr (!last) {
 #pragma unroll
@@ -808,22 +840,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
             store8(xout + i * d.cp + j, v);
             writeback = !QT;                // fp32 also writes X^T from the stage
           } else if (!d.tall) {
-            float wv[8];
-            rw[q].unpack(wv);
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-              v[u] = fmaf(-d.lr, pscale * fmaf(mlt, xv[u], v[u]), wv[u] * wkeep);
-            const int nv = rw_nv[q];
-            const int64_t e0 = i * d.ld + d.col0 + j;
-            GLOBAL float* gw = as_global(w) + e0;
-            if (nv == 8 && (e0 & 3) == 0) {
-              reinterpret_cast<GLOBAL f32x4_t*>(gw)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
-              reinterpret_cast<GLOBAL f32x4_t*>(gw)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
-            } else {
-#pragma unroll
-              for (int u = 0; u < 8; ++u)
-                if (u < nv) gw[u] = v[u];
-            }
+            for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
+            wb[bt & 1][q].update_store(w, i * d.ld + d.col0 + j, wide_nv(i, j), v, d.lr, wkeep);
           } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
@@ -839,18 +858,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     }
     __syncthreads();
     // columns of the tile: C[i .. i+7][j] written as row j of the transpose
-    if (mirror) {
+    auto mirror_vals = [&](int idx, float v[8]) {
+      const int jj = idx / CPC, ch = idx % CPC;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = ch * 8 + u;
+        v[u] = stage[r * SLD + (jj ^ sw(r))];
+      }
+    };
+    if (mirror_w) {
+#pragma unroll
+      for (int mb = 0; mb < MNB; ++mb) {
+        if (mb + 1 < MNB) mprefetch(mb + 1);
+#pragma unroll
+        for (int q = 0; q < MB; ++q) {
+          const int idx = tid + (mb * MB + q) * NT;
+          const int64_t j = j0 + idx / CPC, i = ib0 + (idx % CPC) * 8;
+          float v[8];
+          mirror_vals(idx, v);
+          wb[mb & 1][q].update_store(w, j * d.ld + d.col0 + i, mirror_nv(i, j), v, d.lr, wkeep);
+        }
+      }
+    } else if (mirror) {
 #pragma unroll
       for (int q = 0; q < MIT; ++q) {
         const int idx = tid + q * NT;
-        const int jj = idx / CPC, ch = idx % CPC;
-        const int64_t j = j0 + jj, i = ib0 + ch * 8;
+        const int64_t j = j0 + idx / CPC, i = ib0 + (idx % CPC) * 8;
         float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int r = ch * 8 + u;
-          v[u] = stage[r * SLD + (jj ^ sw(r))];
-        }
+        mirror_vals(idx, v);
         if constexpr (OP == kGemmGram) {
           // the direct pass does not write its scaled values back to the stage
 #pragma unroll
@@ -858,13 +893,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           store8(static_cast<T*>(d.a) + j * d.rp + i, v);
         } else if constexpr (OP == kGemmPoly) {
           store8(static_cast<T*>(d.b) + j * d.rp + i, v);
-        } else {
-          if constexpr (!last) {
-            store8(xtn + j * d.rp + i, v);
-          } else if (j < d.c) {
-            const int nv = int(max<int64_t>(0, min<int64_t>(8, d.r - i)));
-            if (nv > 0) w_update8(w, j * d.ld + d.col0 + i, nv, v, d.lr, wkeep);
-          }
+        } else if constexpr (!last) {
+          store8(xtn + j * d.rp + i, v);
         }
       }
     }
