@@ -34,6 +34,31 @@ __device__ __forceinline__ float4 load_g4(const void* g, int gdt, int64_t idx) {
   return *reinterpret_cast<const float4*>(static_cast<const float*>(g) + idx);
 }
 
+#define GLOBAL __attribute__((address_space(1)))
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float4 ld4(const GLOBAL float* p) {
+  const f32x4v v = *(const GLOBAL f32x4v*)(p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st4(GLOBAL float* p, float4 v) {
+  *(GLOBAL f32x4v*)(p) = f32x4v{v.x, v.y, v.z, v.w};
+}
+
+// Same, with the gradient dtype fixed (0 = f32, 1 = bf16) and global-memory
+// loads (FLAT loads would also count against the LDS/scalar counter).
+template <int GDT>
+__device__ __forceinline__ float4 load_g4t(const void* g, int64_t idx) {
+  if constexpr (GDT == 1) {
+    const u32x2v u = *(const GLOBAL u32x2v*)(static_cast<const uint16_t*>(g) + idx);
+    return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
+                       bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
+  } else {
+    return ld4((const GLOBAL float*)(static_cast<const float*>(g) + idx));
+  }
+}
+
 __device__ __forceinline__ float load_g1(const void* g, int gdt, int64_t idx) {
   if (gdt == 1) return bf16_to_f32(static_cast<const uint16_t*>(g)[idx]);
   return static_cast<const float*>(g)[idx];
@@ -65,6 +90,60 @@ __device__ __forceinline__ int find_mat(const int64_t* prefix, int nmat, int64_t
   return lo;
 }
 
+// One row (n <= MAXCH * 1024, n % 4 == 0) of a wide matrix held in
+// registers: M <- beta M + G, then W <- W (1 - lr wd) - coef M with coef from
+// the row's norm.  Loads are issued ahead of the stores that may alias them
+// (as far as the compiler knows): G, M and, for rows of up to 8 chunks, W
+// all before the reduction; longer rows load W after it, in batches of 8
+// chunks.  Chunks past the row end re-read its last chunk and are not used.
+template <int MAXCH, int GDT>
+__device__ __forceinline__ void rows_in_registers(const void* g, int64_t goff, float* M, float* W,
+                                                  int64_t n, const StepScalars& sc, float* red) {
+  constexpr int WB = MAXCH < 8 ? MAXCH : 8;      // W chunks per batch
+  constexpr bool W_EARLY = MAXCH <= 8;
+  GLOBAL float* gM = (GLOBAL float*)(M);
+  GLOBAL float* gW = (GLOBAL float*)(W);
+  const int tid = threadIdx.x;
+  const float wkeep = 1.0f - sc.lr * sc.wd;
+  float4 gv[MAXCH], mv[MAXCH], wv[WB];
+#pragma unroll
+  for (int ch = 0; ch < MAXCH; ++ch) {
+    const int64_t e = min((int64_t(ch) * kThreads + tid) * 4, n - 4);
+    gv[ch] = load_g4t<GDT>(g, goff + e);
+    mv[ch] = ld4(gM + e);
+  }
+  if constexpr (W_EARLY) {
+#pragma unroll
+    for (int ch = 0; ch < WB; ++ch) wv[ch] = ld4(gW + min((int64_t(ch) * kThreads + tid) * 4, n - 4));
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int ch = 0; ch < MAXCH; ++ch) {
+    mv[ch] = fma4(sc.beta, mv[ch], gv[ch]);
+    if ((int64_t(ch) * kThreads + tid) * 4 < n) ss += dot4(mv[ch]);
+  }
+  const float tot = block_sum(ss, red);
+  const float coef = sc.lr * sc.gamma / fmaxf(sqrtf(tot), sc.eps_row);
+#pragma unroll
+  for (int b = 0; b < MAXCH; b += WB) {
+    if constexpr (!W_EARLY) {
+#pragma unroll
+      for (int u = 0; u < WB; ++u)
+        wv[u] = ld4(gW + min((int64_t(b + u) * kThreads + tid) * 4, n - 4));
+    }
+#pragma unroll
+    for (int u = 0; u < WB; ++u) {
+      const int64_t e = (int64_t(b + u) * kThreads + tid) * 4;
+      if (e < n) {
+        st4(gM + e, mv[b + u]);
+        const float4 w = wv[u];
+        st4(gW + e, fma4(-coef, mv[b + u],
+                         make_float4(w.x * wkeep, w.y * wkeep, w.z * wkeep, w.w * wkeep)));
+      }
+    }
+  }
+}
+
 // One workgroup per row.  MAXCH > 0: the row (<= MAXCH * 1024 elements)
 // stays in registers between the norm and the update.  MAXCH == 0: any
 // length, the updated momentum is re-read for the second pass.
@@ -87,29 +166,8 @@ __global__ __launch_bounds__(kThreads) void rownorm_rows_kernel(
 
   if ((n & 3) == 0) {
     if constexpr (MAXCH > 0) {
-      float4 mv[MAXCH];
-#pragma unroll
-      for (int ch = 0; ch < MAXCH; ++ch) {
-        const int64_t e = (int64_t(ch) * kThreads + tid) * 4;
-        if (e < n) {
-          const float4 g = load_g4(d.g, d.gdt, goff + e);
-          const float4 m = *reinterpret_cast<const float4*>(M + e);
-          mv[ch] = fma4(sc.beta, m, g);
-          ss += dot4(mv[ch]);
-        }
-      }
-      const float tot = block_sum(ss, red);
-      const float coef = sc.lr * sc.gamma / fmaxf(sqrtf(tot), sc.eps_row);
-#pragma unroll
-      for (int ch = 0; ch < MAXCH; ++ch) {
-        const int64_t e = (int64_t(ch) * kThreads + tid) * 4;
-        if (e < n) {
-          *reinterpret_cast<float4*>(M + e) = mv[ch];
-          float4 w = *reinterpret_cast<const float4*>(W + e);
-          w = make_float4(w.x * wkeep, w.y * wkeep, w.z * wkeep, w.w * wkeep);
-          *reinterpret_cast<float4*>(W + e) = fma4(-coef, mv[ch], w);
-        }
-      }
+      if (d.gdt == 1) rows_in_registers<MAXCH, 1>(d.g, goff, M, W, n, sc, red);
+      else rows_in_registers<MAXCH, 0>(d.g, goff, M, W, n, sc, red);
     } else {
       for (int64_t e = int64_t(tid) * 4; e < n; e += kThreads * 4) {
         const float4 g = load_g4(d.g, d.gdt, goff + e);
@@ -136,6 +194,95 @@ __global__ __launch_bounds__(kThreads) void rownorm_rows_kernel(
     const float tot = block_sum(ss, red);
     const float coef = sc.lr * sc.gamma / fmaxf(sqrtf(tot), sc.eps_row);
     for (int64_t e = tid; e < n; e += kThreads) W[e] = fmaf(-coef, M[e], W[e] * wkeep);
+  }
+}
+
+// Tall-matrix row loops, four adjacent columns per thread.  A thread visits
+// rows rb, rb + 4, rb + 8, ... of its tile, in batches of kColBatch such
+// rows: all loads of a batch are issued before any of its stores, so one
+// memory round trip serves the whole batch (the stores may alias the loads as
+// far as the compiler knows, so it would not reorder them itself).  Loads of
+// rows at or past r1 re-read row r1 - 1 (no branch around a load); their
+// stores and sums are skipped.  Sums of squares accumulate in row order.
+constexpr int kColBatch = 8;
+
+template <int GDT>
+__device__ __forceinline__ void cols_fetch_gm(const void* g, const GLOBAL float* mom, int64_t n,
+                                              int64_t col, int64_t rb, int64_t r1,
+                                              float4 (&gv)[kColBatch], float4 (&mv)[kColBatch]) {
+#pragma unroll
+  for (int u = 0; u < kColBatch; ++u) {
+    const int64_t e = min(rb + 4 * u, r1 - 1) * n + col;
+    gv[u] = load_g4t<GDT>(g, e);
+    mv[u] = ld4(mom + e);
+  }
+}
+
+__device__ __forceinline__ void cols_momentum(GLOBAL float* mom, int64_t n, int64_t col, int64_t rb,
+                                              int64_t r1, float beta,
+                                              const float4 (&gv)[kColBatch],
+                                              const float4 (&mv)[kColBatch], float (&ss)[4]) {
+#pragma unroll
+  for (int u = 0; u < kColBatch; ++u) {
+    const int64_t r = rb + 4 * u;
+    if (r < r1) {
+      const float4 mm = fma4(beta, mv[u], gv[u]);
+      st4(mom + r * n + col, mm);
+      ss[0] += mm.x * mm.x; ss[1] += mm.y * mm.y; ss[2] += mm.z * mm.z; ss[3] += mm.w * mm.w;
+    }
+  }
+}
+
+// Phase 1: M <- beta M + G over the thread's rows, sums of squares per column.
+template <int GDT>
+__device__ __forceinline__ void cols_phase1_vec(const MatDev& d, int64_t n, int64_t col,
+                                                int64_t rb, int64_t r1, float beta,
+                                                float (&ss)[4]) {
+  GLOBAL float* mom = (GLOBAL float*)(d.mom);
+  float4 gv[kColBatch], mv[kColBatch];
+  for (; rb < r1; rb += 4 * kColBatch) {
+    cols_fetch_gm<GDT>(d.g, mom, n, col, rb, r1, gv, mv);
+    cols_momentum(mom, n, col, rb, r1, beta, gv, mv, ss);
+  }
+}
+
+__device__ __forceinline__ void cols_fetch_mw(const GLOBAL float* mom, const GLOBAL float* w,
+                                              int64_t n, int64_t col, int64_t rb, int64_t r1,
+                                              float4 (&mv)[kColBatch], float4 (&wv)[kColBatch]) {
+#pragma unroll
+  for (int u = 0; u < kColBatch; ++u) {
+    const int64_t e = min(rb + 4 * u, r1 - 1) * n + col;
+    mv[u] = ld4(mom + e);
+    wv[u] = ld4(w + e);
+  }
+}
+
+__device__ __forceinline__ void cols_update(GLOBAL float* w, int64_t n, int64_t col, int64_t rb,
+                                            int64_t r1, const float (&coef)[4], float wkeep,
+                                            const float4 (&mv)[kColBatch],
+                                            const float4 (&wv)[kColBatch]) {
+#pragma unroll
+  for (int u = 0; u < kColBatch; ++u) {
+    const int64_t r = rb + 4 * u;
+    if (r < r1) {
+      const float4 mm = mv[u], ww = wv[u];
+      st4(w + r * n + col,
+          make_float4(fmaf(-coef[0], mm.x, ww.x * wkeep), fmaf(-coef[1], mm.y, ww.y * wkeep),
+                      fmaf(-coef[2], mm.z, ww.z * wkeep), fmaf(-coef[3], mm.w, ww.w * wkeep)));
+    }
+  }
+}
+
+// Phase 2: W <- W (1 - lr wd) - coef M over the thread's rows.
+__device__ __forceinline__ void cols_phase2_vec(const MatDev& d, int64_t n, int64_t col,
+                                                int64_t rb, int64_t r1, const float (&coef)[4],
+                                                float wkeep) {
+  const GLOBAL float* mom = (const GLOBAL float*)(d.mom);
+  GLOBAL float* w = (GLOBAL float*)(d.w);
+  float4 mv[kColBatch], wv[kColBatch];
+  for (; rb < r1; rb += 4 * kColBatch) {
+    cols_fetch_mw(mom, w, n, col, rb, r1, mv, wv);
+    cols_update(w, n, col, rb, r1, coef, wkeep, mv, wv);
   }
 }
 
@@ -170,14 +317,8 @@ __global__ __launch_bounds__(kThreads) void rownorm_cols_kernel(
     if (vec) {
       const int64_t col = c0 + ct * 4;
       if (col < n) {
-#pragma unroll 8
-        for (int64_t r = r0 + rg; r < r1; r += 4) {
-          const int64_t e = r * n + col;
-          const float4 g = load_g4(d.g, d.gdt, e);
-          const float4 mm = fma4(sc.beta, *reinterpret_cast<const float4*>(d.mom + e), g);
-          *reinterpret_cast<float4*>(d.mom + e) = mm;
-          ss[0] += mm.x * mm.x; ss[1] += mm.y * mm.y; ss[2] += mm.z * mm.z; ss[3] += mm.w * mm.w;
-        }
+        if (d.gdt == 1) cols_phase1_vec<1>(d, n, col, r0 + rg, r1, sc.beta, ss);
+        else cols_phase1_vec<0>(d, n, col, r0 + rg, r1, sc.beta, ss);
       }
     } else {
       for (int64_t r = r0 + rg; r < r1; r += 4) {
@@ -216,17 +357,7 @@ __global__ __launch_bounds__(kThreads) void rownorm_cols_kernel(
     const float wkeep = 1.0f - sc.lr * sc.wd;
     if (vec) {
       const int64_t col = c0 + ct * 4;
-      if (col < n) {
-#pragma unroll 8
-        for (int64_t r = r0 + rg; r < r1; r += 4) {
-          const int64_t e = r * n + col;
-          const float4 mm = *reinterpret_cast<const float4*>(d.mom + e);
-          const float4 w = *reinterpret_cast<const float4*>(d.w + e);
-          *reinterpret_cast<float4*>(d.w + e) =
-              make_float4(fmaf(-coef[0], mm.x, w.x * wkeep), fmaf(-coef[1], mm.y, w.y * wkeep),
-                          fmaf(-coef[2], mm.z, w.z * wkeep), fmaf(-coef[3], mm.w, w.w * wkeep));
-        }
-      }
+      if (col < n) cols_phase2_vec(d, n, col, r0 + rg, r1, coef, wkeep);
     } else {
       for (int64_t r = r0 + rg; r < r1; r += 4) {
 #pragma unroll
