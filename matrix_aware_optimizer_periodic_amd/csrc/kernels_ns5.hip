@@ -77,6 +77,44 @@ __device__ __forceinline__ float load_g(const void* g, int gdt, int64_t idx) {
   return static_cast<const float*>(g)[idx];
 }
 
+// The four rows p0 + tr + 16 pass (pass = 0..3) of a prep tile, four columns
+// each (whole, 16-byte aligned runs): M <- beta M + G, the new values in v.
+// All loads go out before any store; rows at or past `rows` re-read row
+// rows - 1 (no branch around a load), are not stored, and give zeros.  FULL:
+// the whole tile is inside the block, so no row needs those checks (and the
+// stores need no branches, which would make the compiler wait for every
+// load before each of them).
+template <int GDT, bool FULL>
+__device__ __forceinline__ void prep_rows_vec(const MatDev& mt, int64_t ld, int64_t e0,
+                                              int64_t p0, int64_t rows, float beta,
+                                              float (&v)[4][4]) {
+  f32x4_t g[4], m[4];
+  float* mom = mt.mom;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int64_t e = (FULL ? p0 + 16 * pass : min(p0 + 16 * pass, rows - 1)) * ld + e0;
+    if constexpr (GDT == 1) {
+      const u32x2_t u = *as_global(reinterpret_cast<const u32x2_t*>(
+          static_cast<const uint16_t*>(mt.g) + e));
+      g[pass] = f32x4_t{bf16_to_f32(u[0] & 0xffffu), bf16_to_f32(u[0] >> 16),
+                        bf16_to_f32(u[1] & 0xffffu), bf16_to_f32(u[1] >> 16)};
+    } else {
+      g[pass] = *as_global(reinterpret_cast<const f32x4_t*>(static_cast<const float*>(mt.g) + e));
+    }
+    m[pass] = *as_global(reinterpret_cast<const f32x4_t*>(mom + e));
+  }
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int64_t p = p0 + 16 * pass;
+    f32x4_t mm;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mm[u] = fmaf(beta, m[pass][u], g[pass][u]);
+    if (FULL || p < rows) *as_global(reinterpret_cast<f32x4_t*>(mom + p * ld + e0)) = mm;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[pass][u] = (FULL || p < rows) ? mm[u] : 0.f;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Refresh-step preparation, one 64 x 64 tile of the padded stored block per
 // workgroup: M <- beta M + G for the tile's valid elements, the tile's sum of
@@ -104,38 +142,38 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
   const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
   const bool vec = ((d.ld | d.col0) & 3) == 0 && q0 + kPrepTile <= d.cols;
   float ss = 0.f;
+  float vt[4][4];
+  if (vec) {
+    const int64_t e0 = d.col0 + q0 + tc;
+    const bool full = p0 + kPrepTile <= d.rows;
+    if (mt.gdt == 1) {
+      if (full) prep_rows_vec<1, true>(mt, d.ld, e0, p0 + tr, d.rows, beta, vt);
+      else prep_rows_vec<1, false>(mt, d.ld, e0, p0 + tr, d.rows, beta, vt);
+    } else {
+      if (full) prep_rows_vec<0, true>(mt, d.ld, e0, p0 + tr, d.rows, beta, vt);
+      else prep_rows_vec<0, false>(mt, d.ld, e0, p0 + tr, d.rows, beta, vt);
+    }
+  } else {
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int64_t p = p0 + tr + 16 * pass;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        vt[pass][u] = 0.f;
+        const int64_t e = p * d.ld + d.col0 + q0 + tc + u;
+        if (p < d.rows && q0 + tc + u < d.cols) {
+          const float m = fmaf(beta, mt.mom[e], load_g(mt.g, mt.gdt, e));
+          mt.mom[e] = m;
+          vt[pass][u] = m;
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int lr = tr + 16 * pass;
     const int64_t p = p0 + lr;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (p < d.rows) {
-      const int64_t e = p * d.ld + d.col0 + q0 + tc;
-      if (vec) {
-        float4 g;
-        if (mt.gdt == 1) {
-          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(mt.g) + e);
-          g = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
-                          bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
-        } else {
-          g = *reinterpret_cast<const float4*>(static_cast<const float*>(mt.g) + e);
-        }
-        float4 m = *reinterpret_cast<const float4*>(mt.mom + e);
-        m = make_float4(fmaf(beta, m.x, g.x), fmaf(beta, m.y, g.y), fmaf(beta, m.z, g.z),
-                        fmaf(beta, m.w, g.w));
-        *reinterpret_cast<float4*>(mt.mom + e) = m;
-        v[0] = m.x; v[1] = m.y; v[2] = m.z; v[3] = m.w;
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (q0 + tc + u < d.cols) {
-            const float m = fmaf(beta, mt.mom[e + u], load_g(mt.g, mt.gdt, e + u));
-            mt.mom[e + u] = m;
-            v[u] = m;
-          }
-        }
-      }
-    }
+    const float* v = vt[pass];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       ss += v[u] * v[u];
@@ -146,9 +184,9 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
     if constexpr (sizeof(T) == 2) {
       const uint32_t lo = pack_bf16x2(v[0], v[1]);
       const uint32_t hi = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<u32x2_t*>(o) = u32x2_t{lo, hi};
+      *as_global(reinterpret_cast<u32x2_t*>(o)) = u32x2_t{lo, hi};
     } else {
-      *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
+      *as_global(reinterpret_cast<f32x4_t*>(o)) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
   }
   const float tot = block_sum(ss, red);   // contains the barrier the transpose needs
@@ -164,9 +202,9 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
     if constexpr (sizeof(T) == 2) {
       const uint32_t lo = pack_bf16x2(v[0], v[1]);
       const uint32_t hi = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<u32x2_t*>(o) = u32x2_t{lo, hi};
+      *as_global(reinterpret_cast<u32x2_t*>(o)) = u32x2_t{lo, hi};
     } else {
-      *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
+      *as_global(reinterpret_cast<f32x4_t*>(o)) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
   }
 }
