@@ -382,6 +382,18 @@ __device__ __forceinline__ void dma16(u32x4_t rsrc, unsigned lds_addr, unsigned 
       : "m0");
 }
 
+// 4 bytes per lane from a raw buffer straight into LDS (lane l lands at
+// lds_addr + 4 l); same conventions as dma16.
+__device__ __forceinline__ void dma4(u32x4_t rsrc, unsigned lds_addr, unsigned voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "m0");
+}
+
 // Raw buffer resource: base, stride 0, byte size (reads past it return 0).
 __device__ __forceinline__ u32x4_t buffer_rsrc(const void* p, int64_t nbytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(p);
@@ -514,6 +526,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
 #pragma unroll
     for (int b = 0; b < FN; ++b) acc[a][b] = (f32x16_t)(0.0f);
 
+  // QT: the remainders lo_i of this wave's output rows (WM values from
+  // bdiag) come by DMA too, into the ring slot of stage NSTAGE - 1, which is
+  // not filled before the first loop iteration; issued ahead of the stages,
+  // the prologue's wait covers them.  (A plain load here would make the
+  // compiler wait for every DMA in flight before its first use.)
+  constexpr int DLO_SLOT = (NSTAGE - 1) * STAGE;
+  static_assert(!QT || (WM % 64 == 0 && NW * WM * 4 <= STAGE), "dlo staging");
+  if constexpr (QT) {
+    const u32x4_t rD = buffer_rsrc(d.bdiag, d.rp * int64_t(sizeof(float)));
+#pragma unroll
+    for (int h = 0; h < WM / 64; ++h)
+      dma4(rD, unsigned(uintptr_t(smem + DLO_SLOT + (swid * WM + 64 * h) * 4)),
+           unsigned((i0 + wm * WM + 64 * h + lane) * int64_t(sizeof(float))));
+  }
   for (int s0 = 0; s0 < NSTAGE - 1; ++s0) issue(s0);
 
   const int frow = lane & 31, fsw = (lane >> 2) & 3, fhalf = lane >> 5;
@@ -620,13 +646,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // fragment row fa, and the stage that holds those rows of X for fa = 0.
   float dlo[FM];
   const int kf0 = int(it.ti) * (BM / 32) + (swid / WGN) * FM;   // scalar: a uniform branch
-  if constexpr (QT) {
-#pragma unroll
-    for (int fa = 0; fa < FM; ++fa) dlo[fa] = d.bdiag[i0 + wm * WM + fa * 32 + (lane & 31)];
-  }
   {
     wait_vmcnt<(NSTAGE - 2) * DMA>();   // stage 0 is in; stages 1 .. NSTAGE-2 may be in flight
     bar();
+    if constexpr (QT) {
+      const float* sd = reinterpret_cast<const float*>(smem + DLO_SLOT) + wid * WM;
+#pragma unroll
+      for (int fa = 0; fa < FM; ++fa) dlo[fa] = sd[fa * 32 + (lane & 31)];
+    }
     const u32x4_t *sP, *sQ;
     stage_ptrs(0, sP, sQ);
     frag(sP, sQ, 0, a0, b0);
