@@ -164,6 +164,14 @@ def test_ragged_mixed_set(prec):
     run_direction_parity(RAGGED, 6, ns_precision=prec)
 
 
+def test_long_ragged_rows():
+    """Rows longer than 8 K values that end inside a 1024-value chunk: the
+    wide RowNorm kernel's 16- and 32-chunk register variants (W loaded in
+    batches after the row reduction, chunks past the row end re-read and
+    dropped), next to a tall matrix with a ragged last row tile."""
+    run_direction_parity([(3, 9000), (2, 20000), (5, 16388), (1030, 260)], 3, ns_precision=1)
+
+
 def test_edge_values_zero_and_subthreshold_slices():
     """A zero gradient matrix, zero rows, and rows whose norm stays below eps."""
     shapes = [(64, 256), (256, 64), (40, 96)]
