@@ -133,6 +133,9 @@ muon_status muon_config_default(muon_config* out);
 
 /* Bytes of state buffer that muon_init needs for this parameter list.
  * params[i] / kinds[i] (muon_kind) for i < n; n == 0 is a valid empty set.
+ * MUON_E_SHAPE also when a matrix's Newton-Schulz working copy (short side
+ * by long side, padded to the GEMM tile, 2 bytes per value in bf16, 4 in
+ * fp32) reaches 4 GiB: the GEMM kernels address it with 32-bit offsets.
  * Pure host function: touches no device. */
 muon_status muon_state_bytes(const muon_config* cfg, const muon_tensor* params,
                              const int32_t* kinds, int32_t n, size_t* bytes);

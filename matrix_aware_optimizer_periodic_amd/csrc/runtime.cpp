@@ -348,12 +348,20 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
   }
   pl.ns_full = plan_ns(full, cfg);
   pl.ns_block = plan_ns(block, cfg);
+  // The GEMM kernels address X (rp x cp) and A, B (rp x rp) through raw
+  // buffer descriptors with 32-bit byte sizes and offsets.
+  const int64_t ns_es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
   for (auto* plan : {&pl.ns_full, &pl.ns_block})
     for (NsChunk& ch : *plan)
-      for (const NsDev& d : ch.ns)
+      for (const NsDev& d : ch.ns) {
         if (d.rp / 128 > 32767 || d.cp / 64 > 32767) {
           err = "matrix too large for the tile index range"; return MUON_E_SHAPE;
         }
+        if (d.rp * d.cp * ns_es >= (int64_t(1) << 32)) {
+          err = "matrix too large: its Newton-Schulz workspace copy exceeds 4 GiB";
+          return MUON_E_SHAPE;
+        }
+      }
   // 5. tables
   pl.off_mats = bump.take(pl.mats.size() * sizeof(MatDev));
   pl.off_adams = bump.take(pl.adams.size() * sizeof(AdamDev));

@@ -133,6 +133,20 @@ def test_muonbp_split_must_be_even():
     assert m.muon_state_bytes(c, [desc(64, 48)], [0]) > 0
 
 
+def test_workspace_matrix_over_4gib_is_rejected():
+    """X (r x c, padded) is addressed with 32-bit buffer offsets: a matrix
+    whose workspace copy reaches 4 GiB must fail planning, not run wrong."""
+    with pytest.raises(m.MuonError) as e:
+        m.muon_state_bytes(m.muon_config_default(), [desc(40000, 60000)], [0])
+    assert e.value.status == m.binding.MUON_E_SHAPE
+    assert "4 GiB" in m.muon_last_error()
+    # just under the limit in bf16, over it in fp32
+    assert m.muon_state_bytes(m.muon_config_default(), [desc(32768, 65000)], [0]) > 0
+    with pytest.raises(m.MuonError):
+        m.muon_state_bytes(m.muon_config_default(ns_precision=m.MUON_NS_F32),
+                           [desc(32768, 65000)], [0])
+
+
 def test_unknown_kind():
     with pytest.raises(m.MuonError) as e:
         m.muon_state_bytes(m.muon_config_default(), [desc(4, 4)], [9])
