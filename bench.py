@@ -73,13 +73,14 @@ def cnt_per(name: str, cfg) -> int:
 
 
 def source_digest() -> str:
-    """sha256 over the library's sources (csrc/), so that counter figures
-    taken on other sources are not reported."""
+    """sha256 over the device code (csrc/*.hip and the header they share),
+    so that counter figures taken on other kernels are not reported.  Host
+    code (the launch planner) is left out: the counters follow the kernels."""
     import hashlib
     d = os.path.join(HERE, "matrix_aware_optimizer_periodic_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
+        if f.endswith((".hip", ".h")):
             h.update(f.encode())
             h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()
