@@ -146,18 +146,35 @@ def cpu_baseline(wl, cfg_over, sample_blocks=1):
     M = [np.zeros(s) for s in shapes]
     G = [workloads.host_grad(0, 0, i, s, wl.grad_std, wl.grad_dtype) for i, s in enumerate(shapes)]
     K = ocfg.K if ocfg.bp_blocks == 0 else ocfg.bp_period
-    t0 = time.perf_counter()
-    for t in range(K):
-        for i in range(len(shapes)):
-            W[i], M[i], _ = oracle.muon_matrix_step(W[i], M[i], G[i], t, ocfg)
-    dt = time.perf_counter() - t0
+
+    def cycles():
+        """Whole K-cycles (at least one, more while under a second) -> s/cycle."""
+        n, t0 = 0, time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < 1.0:
+            for t in range(K):
+                for i in range(len(shapes)):
+                    W[i], M[i], _ = oracle.muon_matrix_step(W[i], M[i], G[i], t, ocfg)
+            n += 1
+        return (time.perf_counter() - t0) / n, n
+
+    dt, ncyc = cycles()
     scale = (wl.blocks / sample_blocks) if wl.blocks else 1.0
     steps_per_s = K / (dt * scale)
-    return {"value": steps_per_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "cpu": cpu_model, "blas": blas, "numpy": np.__version__,
-            "sample": f"{len(shapes)} matrices ({sample_blocks} of {wl.blocks or 1} blocks), one "
-                      f"{K}-step cycle, {dt:.1f} s, scaled x{scale:g} to the whole set",
-            "sample_seconds": dt}
+    out = {"value": steps_per_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+           "cpu": cpu_model, "blas": blas, "numpy": np.__version__,
+           "sample": f"{len(shapes)} matrices ({sample_blocks} of {wl.blocks or 1} blocks), "
+                     f"{K}-step cycle x{ncyc}, {dt:.3g} s per cycle, scaled x{scale:g} to the whole set",
+           "sample_seconds": dt * ncyc}
+    if not wl.blocks:
+        # the single-matrix set is small enough to time on one core as well
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                dt1, _ = cycles()
+            out["value_1core"] = K / dt1
+        except Exception:
+            pass
+    return out
 
 
 def copy_calibration(nbytes: int, reps: int) -> None:

@@ -195,6 +195,17 @@ def test_rownorm_stored_rows_mode():
     run_direction_parity([(512, 96), (96, 512), (257, 31)], 3, rownorm_axis=1)
 
 
+@pytest.mark.parametrize("prec", [0, 1])
+def test_other_ns_coefficients_and_iterations(prec):
+    """A recorded variant: the convergent quintic (15/8, -5/4, 3/8) with 8
+    iterations instead of the default coefficients and 5; also 3 iterations
+    of the defaults.  The library takes them from the config like the oracle."""
+    shapes = [(256, 640), (640, 256), (300, 700)]
+    run_direction_parity(shapes, 2, ns_a=1.875, ns_b=-1.25, ns_c=0.375, ns_iters=8,
+                         ns_precision=prec)
+    run_direction_parity(shapes, 1, ns_iters=3, ns_precision=prec)
+
+
 def test_vanilla_muon_K1():
     run_direction_parity([(256, 640), (640, 256)], 3, K=1, ns_precision=1)
 
