@@ -140,6 +140,7 @@ def cpu_baseline(wl, cfg_over, sample_blocks=1):
     except OSError:
         pass
     ocfg = oracle.OracleConfig(**cfg_over)
+    sample_blocks = min(sample_blocks, wl.blocks or 1)
     per_block = len(workloads.dit_block_shapes(wl.d)) if wl.d else len(wl.shapes)
     shapes = [(m, n) for _, m, n in wl.shapes[:per_block * sample_blocks]]
     W = [workloads.host_weight0(0, i, s).astype(np.float64) for i, s in enumerate(shapes)]
