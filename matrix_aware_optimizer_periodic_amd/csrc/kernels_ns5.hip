@@ -400,7 +400,7 @@ __device__ __forceinline__ u32x4_t buffer_rsrc(const void* p, int64_t nbytes) {
   return u32x4_t{unsigned(a), unsigned(a >> 32) & 0xffffu, unsigned(nbytes), 0x00020000u};
 }
 
-template <typename T, int BM, int WGM, int WGN, int OP>
+template <typename T, int BM, int WGM, int WGN, int OP, int BN = BM>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
     const GemmItem* __restrict__ items, int iter, float ca, float cb, float cc,
@@ -413,26 +413,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   constexpr bool QT = PROD && sizeof(T) == 2;
   constexpr int NW = WGM * WGN;
   constexpr int NT = 64 * NW;                // threads
-  constexpr int WM = BM / WGM, WN = BM / WGN;
+  // Output tiles are BM x BN: square except for the bf16 product, which may
+  // take wider tiles (more flops per staged byte).
+  static_assert(BN == BM || (OP == kGemmProduct && sizeof(T) == 2), "wide tiles: bf16 product");
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int ROWS = 2 * BM;               // P rows then Q rows
+  constexpr int ROWS = BM + BN;              // P rows then Q rows (64 bytes each)
   // Stages in the LDS ring: 4 for 256-tiles (of 160 KB), 5 for 128-tiles
   // (80 KB, two workgroups per CU); deeper rings measured no faster.
-  constexpr int NSTAGE = BM >= 256 ? 4 : 5;
+  constexpr int NSTAGE = BM >= 256 ? 4 : BN > BM ? 3 : 5;
   constexpr int STAGE = ROWS * 64;           // bytes per stage
   constexpr int BLOCKS = ROWS / 16;          // 16-row (1 KB) DMA blocks per stage
   constexpr int DMA = BLOCKS / NW;           // DMA instructions per wave per stage
+  constexpr int DMAP = BM / 16 / NW;         // of which for P
   constexpr int KT = 64 / int(sizeof(T));    // k elements per stage
-  constexpr int SLD = BM + 4;                // epilogue stage row stride (floats)
-  // Epilogue rows per pass: the whole tile when its fp32 stage fits the LDS
-  // ring (128-tiles), else half of it.
-  constexpr int NPASS = BM >= 256 ? 2 : 1;
+  constexpr int SLD = BN + 4;                // epilogue stage row stride (floats)
+  // Epilogue rows per pass: as many as the fp32 stage fits in the workgroup's
+  // LDS share (160 KB for 256-tiles, 80 KB for 128-tiles, two per CU).
+  constexpr int LDS_MAX = (BM >= 256 ? 160 : 80) * 1024;
+  constexpr int NPASS = BM * SLD * 4 <= LDS_MAX ? 1 : (BM / 2) * SLD * 4 <= LDS_MAX ? 2 : 4;
   constexpr int HALF = BM / NPASS;
   constexpr int MAIN_BYTES = NSTAGE * STAGE;
   constexpr int STAGE_BYTES = HALF * SLD * 4;
   constexpr int SMEM = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
-  static_assert(WM <= HALF && HALF % WM == 0, "a wave's rows must sit in one half");
-  static_assert(BLOCKS % NW == 0 && DMA % 2 == 0, "whole DMA blocks per wave, half P half Q");
+  static_assert(HALF % 32 == 0 && MAIN_BYTES <= LDS_MAX, "whole 32-row blocks per pass");
+  static_assert((BM / 16) % NW == 0 && (BN / 16) % NW == 0, "whole DMA blocks per wave");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   const u32x4_t* lds = reinterpret_cast<const u32x4_t*>(smem);
 
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
       Q = static_cast<const T*>(cur ? d.xt[1] : d.xt[0]); ldq = d.rp;   // X^T, rows j
     }
   }
-  const int64_t i0 = int64_t(it.ti) * BM, j0 = int64_t(it.tj) * BM;
+  const int64_t i0 = int64_t(it.ti) * BM, j0 = int64_t(it.tj) * BN;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
   const int nk = int(K / KT);
@@ -467,21 +472,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // DMA mapping.  Instruction q of wave w fills LDS rows 16 b .. 16 b + 15 of
   // the stage, b = w + NW q; lane l brings row 16 b + (l >> 2), logical chunk
   // (l & 3) ^ ((l >> 4) & 3), which lands at physical chunk l & 3.
-  // Blocks q < DMA/2 are P rows, the others Q rows.  The loads are MUBUF
+  // Blocks q < DMAP are P rows, the others Q rows.  The loads are MUBUF
   // buffer loads into LDS: unlike the FLAT form they count only against the
   // vector-memory counter, so waiting for LDS fragment reads does not also
   // wait for the prefetch in flight.  Offsets past a buffer's end read 0.
   //
-  // QT: the Q part of a stage is X rows k .. k + 31, columns j0 .. j0 + BM - 1
-  // (2 BM bytes per row, CPRQ 16-byte chunks); DMA block b holds rows
+  // QT: the Q part of a stage is X rows k .. k + 31, columns j0 .. j0 + BN - 1
+  // (2 BN bytes per row, CPRQ 16-byte chunks); DMA block b holds rows
   // RPB b .. RPB b + RPB - 1 and lane l brings row RPB b + l / CPRQ, logical
   // chunk (l % CPRQ) ^ ((row & 3) << 2), which lands at physical chunk
   // l % CPRQ.  The XOR puts the four rows a transposed read touches in four
   // distinct 64-byte bank groups.
   const int drow = 16 * wid + (lane >> 2);
   const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  constexpr int CPRQ = BM / 8, RPB = 64 / CPRQ;
-  static_assert(!QT || (RPB * NW) % 4 == 0, "row phase of a lane fixed across its blocks");
+  constexpr int CPRQ = BN / 8, RPB = 64 / CPRQ;
+  static_assert(!QT || (RPB * CPRQ == 64 && (RPB * NW) % 4 == 0),
+                "whole rows per DMA block; row phase of a lane fixed across its blocks");
   const int qtrow = RPB * wid + lane / CPRQ;
   const int qtchunk = (lane % CPRQ) ^ ((qtrow & 3) << 2);
   const int64_t prow = d.rp;   // P is X, A or B: rp rows
@@ -508,12 +514,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   const int swid = __builtin_amdgcn_readfirstlane(wid);
   auto issue_one = [&](int kt, int q) {
     const int kc = min(kt, nk - 1);
-    const int kb = q < DMA / 2 ? kc * 64 : int(kc * kstepQ);
     LOCAL unsigned char* base =
         (LOCAL unsigned char*)(smem + (kt % NSTAGE) * STAGE + swid * 1024);
-    const unsigned voff = q < DMA / 2 ? offP + unsigned(q) * rstride
-                                      : offQ + unsigned(q - DMA / 2) * rstrideQ;
-    dma16(q < DMA / 2 ? rP : rQ, unsigned(uintptr_t(base + q * NW * 1024)), voff, unsigned(kb));
+    const int kb = q < DMAP ? kc * 64 : int(kc * kstepQ);
+    const unsigned voff = q < DMAP ? offP + unsigned(q) * rstride
+                                   : offQ + unsigned(q - DMAP) * rstrideQ;
+    dma16(q < DMAP ? rP : rQ, unsigned(uintptr_t(base + q * NW * 1024)), voff, unsigned(kb));
   };
   auto issue = [&](int kt) {
 #pragma unroll
@@ -557,7 +563,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   auto qtr = [&](const u32x4_t* sQ, int g, int f, int h, u32x4_t& out) {
     const int row = 16 * g + 4 * h + trow;
     const int col = wn * WN + f * 32 + tcol;
-    const int byte = row * (2 * BM) + (((col >> 3) ^ tsw) << 4) + ((col & 7) << 1);
+    const int byte = row * (2 * BN) + (((col >> 3) ^ tsw) << 4) + ((col & 7) << 1);
     const LOCAL bf16x4_raw_t* p =
         (const LOCAL bf16x4_raw_t*)((const LOCAL unsigned char*)sQ + byte);
     const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -756,11 +762,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // Round 0 works on the unscaled M: A = s^2 (M M^T), X_1 = s (a M + B M).
   const float s0 = iter == 0 ? d.scale[0] : 1.0f;
   const float gscale = s0 * s0, pscale = s0;
-  constexpr int CPR = BM / 8;                  // 8-value chunks per tile row
+  constexpr int CPR = BN / 8;                  // 8-value chunks per tile row
   constexpr int DIT = HALF * CPR / NT;         // direct-pass chunks per thread
   constexpr int CPC = HALF / 8;                // 8-value chunks per mirrored row
-  constexpr int MIT = BM * CPC / NT;           // mirror-pass chunks per thread
-  static_assert(DIT * NT == HALF * CPR && MIT * NT == BM * CPC, "whole passes");
+  constexpr int MIT = BN * CPC / NT;           // mirror-pass chunks per thread
+  static_assert(DIT * NT == HALF * CPR && MIT * NT == BN * CPC, "whole passes");
   // The direct pass needs operand reads per chunk (A for B; X for the
   // product, plus W for the last product of a wide matrix).  They are issued in
   // batches of PB chunks, double-buffered: batch bt + 1 is in flight while
@@ -820,18 +826,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     };
     if (need_aux) prefetch(0);
     if (mirror_w) mprefetch(0);
-    if (wm * WM >= half * HALF && wm * WM < (half + 1) * HALF) {
-      const int rbase = wm * WM - half * HALF;
 #pragma unroll
-      for (int fa = 0; fa < FM; ++fa)
+    for (int fa = 0; fa < FM; ++fa) {
+      const int rb = wm * WM + fa * 32 - half * HALF;   // block row fa, first row in this pass
+      if (rb >= 0 && rb < HALF) {
 #pragma unroll
         for (int fb = 0; fb < FN; ++fb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int r = rbase + fa * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3);
+            const int r = rb + 8 * (v >> 2) + 4 * fhalf + (v & 3);
             const int c = wn * WN + fb * 32 + frow;
             stage[r * SLD + (c ^ sw(r))] = acc[fa][fb][v];
           }
+      }
     }
     __syncthreads();
     // rows of the tile: C[i][j .. j+7]
@@ -972,12 +979,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
 // holds its 128 x 128 accumulators in the 256 AGPRs.
 template <int BM, int OP> struct WaveGrid { static constexpr int M = 2, N = 2; };
 
-template <typename T, int BM, int OP>
+template <typename T, int BM, int OP, int BN = BM>
 void launch_gemm_op(hipStream_t s, const MatDev* mats, const NsDev* ns, const GemmItem* items,
                     int64_t nitems, int iter, float a, float b, float c, float wd) {
   constexpr int GM = WaveGrid<BM, OP>::M, GN = WaveGrid<BM, OP>::N;
-  ns_gemm_kernel<T, BM, GM, GN, OP><<<dim3(static_cast<unsigned>(nitems)), dim3(64 * GM * GN), 0, s>>>(
-      mats, ns, items, iter, a, b, c, wd);
+  ns_gemm_kernel<T, BM, GM, GN, OP, BN>
+      <<<dim3(static_cast<unsigned>(nitems)), dim3(64 * GM * GN), 0, s>>>(mats, ns, items, iter, a,
+                                                                          b, c, wd);
 }
 
 template <typename T, int BM>
@@ -1021,9 +1029,18 @@ hipError_t launch_ns_scale(hipStream_t s, NsDev* ns_dev, int32_t count, float ep
 }
 
 hipError_t launch_ns_gemm(hipStream_t s, const MatDev* mats, const NsDev* ns,
-                          const GemmItem* items, int64_t nitems, int op, int tile, int prec,
-                          int iter, int last, float a, float b, float c, float wd) {
+                          const GemmItem* items, int64_t nitems, int op, int tile, int tile_n,
+                          int prec, int iter, int last, float a, float b, float c, float wd) {
   if (nitems <= 0) return hipSuccess;
+  if (tile_n != tile) {
+    // the one wide tile: 128 x 256 for the bf16 product of the rounds
+    // before the last (short K: twice the work per tile prologue/epilogue
+    // and a third fewer staged bytes per flop than 128 x 128)
+    if (prec != 0 || tile != 128 || tile_n != 256 || op != kGemmProduct || last)
+      return hipErrorInvalidValue;
+    launch_gemm_op<uint16_t, 128, kGemmProduct, 256>(s, mats, ns, items, nitems, iter, a, b, c, wd);
+    return hipGetLastError();
+  }
   if (prec == 0) {
     if (tile == 256) return launch_gemm_t<uint16_t, 256>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
     return launch_gemm_t<uint16_t, 128>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);

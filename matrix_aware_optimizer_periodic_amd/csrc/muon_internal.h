@@ -109,8 +109,10 @@ hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem
 hipError_t launch_ns_prep(hipStream_t s, const MatDev* mats, const NsDev* ns,
                           const TileItem* items, int64_t nitems, int prec, float beta);
 hipError_t launch_ns_scale(hipStream_t s, NsDev* ns_dev, int32_t count, float eps);
+// tile x tile_n output tiles (tile_n != tile only for 128 x 256 bf16
+// products of the rounds before the last).
 hipError_t launch_ns_gemm(hipStream_t s, const MatDev* mats, const NsDev* ns,
-                          const GemmItem* items, int64_t nitems, int op, int tile,
+                          const GemmItem* items, int64_t nitems, int op, int tile, int tile_n,
                           int prec, int iter, int last, float a, float b, float c, float wd);
 hipError_t launch_adamw(hipStream_t s, const AdamDev* t, const AdamChunk* chunks,
                         int64_t nchunks, float lr, float b1, float b2, float eps,

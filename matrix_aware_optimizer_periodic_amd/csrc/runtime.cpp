@@ -52,6 +52,8 @@ struct NsChunk {
   std::vector<size_t> ws_off;     // per problem: workspace offset (relative to ws base)
   std::vector<TileItem> prep_items;
   GemmList gemm[3][2];            // [op][tile == 256]
+  GemmList prod_wide;             // bf16, 128-tile problems: 128 x 256 product tiles
+                                  // for the rounds before the last
   size_t off_ns = 0, off_prep = 0;
   size_t ws_bytes = 0;
 };
@@ -179,10 +181,15 @@ struct Problem {
   float lr;
 };
 
+// Column padding of X: the tile, or 256 for bf16 128-tile problems, whose
+// products before the last round use 128 x 256 tiles.
+int col_tile(int tile, size_t es) { return tile == 128 && es == 2 ? 256 : tile; }
+
 size_t problem_ws_bytes(const Problem& p, int tile, size_t es, int64_t* rp_out, int64_t* cp_out,
                         int32_t* nparts_out) {
   const int64_t r = std::min(p.rows, p.cols), c = std::max(p.rows, p.cols);
-  const int64_t rp = ceil_div(r, tile) * tile, cp = ceil_div(c, tile) * tile;
+  const int ct = col_tile(tile, es);
+  const int64_t rp = ceil_div(r, tile) * tile, cp = ceil_div(c, ct) * ct;
   const int32_t nparts = static_cast<int32_t>((rp / kPrepTile) * (cp / kPrepTile));
   *rp_out = rp; *cp_out = cp; *nparts_out = nparts;
   size_t b = 0;
@@ -251,6 +258,14 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
           for (int64_t i = ib; i < std::min(nr, ib + kSuperRows); ++i)
             for (int64_t j = jb; j < std::min(nc, jb + kSuperCols); ++j)
               ch.gemm[kGemmProduct][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+      if (col_tile(tile, es) != tile) {
+        const int64_t ncw = d.cp / col_tile(tile, es);
+        for (int64_t jb = 0; jb < ncw; jb += kSuperCols)
+          for (int64_t ib = 0; ib < nr; ib += kSuperRows)
+            for (int64_t i = ib; i < std::min(nr, ib + kSuperRows); ++i)
+              for (int64_t j = jb; j < std::min(ncw, jb + kSuperCols); ++j)
+                ch.prod_wide.items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+      }
     }
     // A tile costs its K: cp for the Gram, rp for the polynomial and product.
     for (int op = 0; op < 3; ++op)
@@ -258,6 +273,7 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
         xcd_interleave(gl.items, [&](const GemmItem& g) {
           return op == kGemmGram ? ch.ns[g.ns].cp : ch.ns[g.ns].rp;
         });
+    xcd_interleave(ch.prod_wide.items, [&](const GemmItem& g) { return ch.ns[g.ns].rp; });
   }
   return chunks;
 }
@@ -379,6 +395,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
       ch.off_prep = bump.take(ch.prep_items.size() * sizeof(TileItem));
       for (auto& op : ch.gemm)
         for (auto& gl : op) gl.off = bump.take(gl.items.size() * sizeof(GemmItem));
+      ch.prod_wide.off = bump.take(ch.prod_wide.items.size() * sizeof(GemmItem));
       ws = std::max(ws, ch.ws_bytes);
     }
   // 6. NS workspace, shared by all chunks of both plans
@@ -545,13 +562,15 @@ muon_status run_ns(muon_ctx* ctx, std::vector<NsChunk>& chunks) {
       const int last = it == c.ns_iters - 1;
       for (int op = 0; op < 3; ++op)
         for (int t = 0; t < 2; ++t) {
-          const GemmList& gl = ch.gemm[op][t];
+          // before the last round, bf16 128-tile products run on 128 x 256 tiles
+          const bool wide = op == kGemmProduct && t == 0 && !last && !ch.prod_wide.items.empty();
+          const GemmList& gl = wide ? ch.prod_wide : ch.gemm[op][t];
           if (gl.items.empty()) continue;
           const GemmItem* items = reinterpret_cast<const GemmItem*>(ctx->base + gl.off);
           MUON_HIP(ctx, MUON_TIMED(ctx, op == 2 && last ? MUON_K_NS_PRODUCT_LAST : MUON_K_NS_GRAM + op,
                                    launch_ns_gemm(ctx->stream, mats, ns, items,
                                                   int64_t(gl.items.size()), op, t ? 256 : 128,
-                                                  prec, it, last, c.ns_a, c.ns_b, c.ns_c,
+                                                  wide ? 256 : (t ? 256 : 128), prec, it, last, c.ns_a, c.ns_b, c.ns_c,
                                                   c.muon_wd)));
         }
     }
@@ -676,6 +695,8 @@ muon_status muon_init(muon_ctx** out, const muon_config* cfg, const muon_tensor*
       for (auto& op : ch.gemm)
         for (auto& gl : op)
           if ((e = upload(ctx, gl.off, gl.items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
+      if ((e = upload(ctx, ch.prod_wide.off, ch.prod_wide.items)) != hipSuccess)
+        return fail(e, "hipMemcpyAsync(ns)");
     }
   // The host copies of the tables must outlive the transfers.
   if ((e = hipStreamSynchronize(ctx->stream)) != hipSuccess) return fail(e, "hipStreamSynchronize");
