@@ -319,14 +319,15 @@ template <> struct Raw8<float> {
   }
 };
 
-// GEMM tile C[i0.., j0..] = sum_k P[i][k] Q[j][k] on MFMA, BM x BM per
-// workgroup of 2 x 2 waves (one per SIMD), each wave (BM/2) x (BM/2) built
+// GEMM tile C[i0.., j0..] = sum_k P[i][k] Q[j][k] on MFMA, BM x BN per
+// workgroup of 2 x 2 waves (one per SIMD), each wave (BM/2) x (BN/2) built
 // from 32 x 32 MFMA blocks; a 256-tile wave holds its 128 x 128 fp32
-// accumulators in the 256 AGPRs.
+// accumulators in the 256 AGPRs.  BN = BM except for the 128 x 256 bf16
+// product tiles of short-K problems.
 //
 // Operand staging.  The k loop runs over stages of 64 bytes of k (32 bf16 or
-// 16 fp32) for all 2 BM rows of P and Q, NSTAGE stages deep in LDS (as many
-// 4 for 256-tiles, 5 for 128-tiles).  Global data goes straight to LDS (MUBUF
+// 16 fp32) for all BM + BN rows of P and Q, NSTAGE stages deep in LDS (4 for
+// 256-tiles, 5 for 128-tiles, 3 for 128 x 256).  Global data goes straight to LDS (MUBUF
 // buffer_load ... lds: each lane's 16 bytes land at the wave's LDS base +
 // 16 * lane), issued NSTAGE - 1 stages ahead of its use, so no registers
 // hold operands in flight.  A 64-byte LDS row holds four 16-byte chunks;
@@ -343,9 +344,9 @@ template <> struct Raw8<float> {
 // between the two operands is valid as long as it is the same for both.
 // Accumulator element v of lane l is C[8 (v/4) + 4 (l/32) + (v%4)][l & 31].
 //
-// Epilogue, per pass over the tile (whole for 128-tiles, halves for
-// 256-tiles): the owning waves park their
-// accumulators in LDS, then all threads write the outputs in 16-byte chunks,
+// Epilogue, per pass over rows of the tile (as many as the workgroup's LDS
+// share holds in fp32): the waves owning them park their accumulators in
+// LDS, then all threads write the outputs in 16-byte chunks,
 // first along rows (C, or W of a wide matrix), then along columns (the
 // mirrored half of a symmetric A or B, X^T in fp32, or W of a tall matrix).
 //
@@ -420,7 +421,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int ROWS = BM + BN;              // P rows then Q rows (64 bytes each)
   // Stages in the LDS ring: 4 for 256-tiles (of 160 KB), 5 for 128-tiles
-  // (80 KB, two workgroups per CU); deeper rings measured no faster.
+  // and 3 for 128 x 256 (within 80 KB: two workgroups per CU); deeper rings
+  // measured no faster.
   constexpr int NSTAGE = BM >= 256 ? 4 : BN > BM ? 3 : 5;
   constexpr int STAGE = ROWS * 64;           // bytes per stage
   constexpr int BLOCKS = ROWS / 16;          // 16-row (1 KB) DMA blocks per stage
