@@ -7,9 +7,11 @@
 // are columns: the post's section "distributed co-design", paper Eq. (8),
 // normalises them by column sums of squares over the rows.
 //
-// Both kernels are HBM-bound: per element they read G (2 or 4 B), M (4 B)
-// and W (4 B) and write M (4 B) and W (4 B).  Reductions run in a fixed
-// order, so results are bitwise reproducible from run to run.
+// The row and column kernels are HBM-bound: per element they read G (2 or
+// 4 B), M (4 B) and W (4 B) and write M (4 B) and W (4 B).  Each thread issues
+// its loads in batches ahead of the stores that may alias them, so a memory
+// round trip serves many rows.  Reductions run in a fixed order, so results
+// are bitwise reproducible from run to run.
 #include <hip/hip_runtime.h>
 
 #include "muon_internal.h"
