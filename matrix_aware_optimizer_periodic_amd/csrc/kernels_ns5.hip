@@ -828,18 +828,35 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     };
     if (need_aux) prefetch(0);
     if (mirror_w) mprefetch(0);
+    if constexpr (WM <= HALF) {
+      // a wave's rows sit in one pass: one test per wave
+      if (wm * WM >= half * HALF && wm * WM < (half + 1) * HALF) {
+        const int rbase = wm * WM - half * HALF;
 #pragma unroll
-    for (int fa = 0; fa < FM; ++fa) {
-      const int rb = wm * WM + fa * 32 - half * HALF;   // block row fa, first row in this pass
-      if (rb >= 0 && rb < HALF) {
+        for (int fa = 0; fa < FM; ++fa)
 #pragma unroll
-        for (int fb = 0; fb < FN; ++fb)
+          for (int fb = 0; fb < FN; ++fb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = rb + 8 * (v >> 2) + 4 * fhalf + (v & 3);
-            const int c = wn * WN + fb * 32 + frow;
-            stage[r * SLD + (c ^ sw(r))] = acc[fa][fb][v];
-          }
+            for (int v = 0; v < 16; ++v) {
+              const int r = rbase + fa * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3);
+              const int c = wn * WN + fb * 32 + frow;
+              stage[r * SLD + (c ^ sw(r))] = acc[fa][fb][v];
+            }
+      }
+    } else {
+#pragma unroll
+      for (int fa = 0; fa < FM; ++fa) {
+        const int rb = wm * WM + fa * 32 - half * HALF;   // block row fa, first row in this pass
+        if (rb >= 0 && rb < HALF) {
+#pragma unroll
+          for (int fb = 0; fb < FN; ++fb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = rb + 8 * (v >> 2) + 4 * fhalf + (v & 3);
+              const int c = wn * WN + fb * 32 + frow;
+              stage[r * SLD + (c ^ sw(r))] = acc[fa][fb][v];
+            }
+        }
       }
     }
     __syncthreads();
