@@ -106,17 +106,25 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def rownorm_class_bytes(shapes, gbytes):
-    """Algorithmic bytes per RowNorm step per kernel class (long-axis mode)."""
-    rows = cols1 = cols2 = 0
+def rownorm_class_bytes(shapes, gbytes, single_pass=True):
+    """Algorithmic bytes per RowNorm step per kernel class (long-axis mode).
+
+    Tall matrices with even n and at most 32768 rows take the single-pass
+    kernel when it is enabled (read G, M, W; write M, W), the others the two
+    passes (G, M -> M, then M, W -> W)."""
+    rows = cols1 = cols2 = tall = 0
     for m, n in shapes:
         e = m * n
         if m > n:
-            cols1 += (gbytes + 8) * e      # read G, M; write M
-            cols2 += 12 * e                # read M, W; write W
+            if single_pass and n % 2 == 0 and m <= 32768:
+                tall += (gbytes + 16) * e
+            else:
+                cols1 += (gbytes + 8) * e      # read G, M; write M
+                cols2 += 12 * e                # read M, W; write W
         else:
             rows += (gbytes + 16) * e
-    return {"rownorm_rows": rows, "rownorm_cols1": cols1, "rownorm_cols2": cols2}
+    return {"rownorm_rows": rows, "rownorm_cols1": cols1, "rownorm_cols2": cols2,
+            "rownorm_tall": tall}
 
 
 def cpu_baseline(wl, cfg_over, sample_blocks=1):
@@ -203,6 +211,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample-blocks", type=int, default=2)
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--ws-gib", type=float, default=None, help="NS5 workspace cap (GiB)")
+    ap.add_argument("--tall-two-pass", action="store_true",
+                    help="tall RowNorm in two passes instead of one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter scaling)")
     args = ap.parse_args()
@@ -225,6 +235,8 @@ def main() -> int:
     if args.K is not None:
         over["K"] = args.K
     over["ns_precision"] = mm.MUON_NS_BF16 if args.ns_precision == "bf16" else mm.MUON_NS_F32
+    if args.tall_two_pass:
+        over["tall_single_pass"] = 0
     if args.ws_gib is not None:
         over["ns_workspace_max"] = int(args.ws_gib * 2 ** 30)
     cfg = mm.muon_config_default(**over)
@@ -337,7 +349,7 @@ def main() -> int:
     roofline = None
     kernels = {}
     if kt:
-        nb = rownorm_class_bytes(shapes, gbytes)
+        nb = rownorm_class_bytes(shapes, gbytes, bool(cfg.tall_single_pass))
         nsb = ns5_class_bytes(shapes, 2 if args.ns_precision == "bf16" else 4)
         n_rn = branches.count(mm.MUON_BRANCH_ROWNORM)
         for name, (ms, cnt) in kt.items():
@@ -396,6 +408,7 @@ def main() -> int:
                                                     round(cfg.ns_c, 6)],
             "ns_eps": cfg.ns_eps, "ns_prenorm": "X / (||X||_F + ns_eps)",
             "ns_precision": args.ns_precision, "rownorm_axis": "long" if cfg.rownorm_axis == 0 else "rows",
+            "tall_rownorm": "single-pass" if cfg.tall_single_pass else "two-pass",
             "bp_blocks": cfg.bp_blocks, "adamw_tensors": n_bias, "adamw_elements": bias_elems,
             "ns_workspace_max": int(cfg.ns_workspace_max), "state_bytes": sess.state_bytes,
         },

@@ -124,6 +124,16 @@ typedef struct muon_config {
   float adam_lr, adam_b1, adam_b2, adam_eps, adam_wd;
                          /* (1e-3, 0.9, 0.999, 1e-8, 0)                     */
   uint64_t ns_workspace_max; /* cap on NS5 workspace bytes; 0 = no cap     */
+  int32_t tall_single_pass; /* 1 (default): long-axis RowNorm of a tall
+                          * matrix (m > n, n even, m <= 32768) runs as
+                          * one pass over its tensors, with the column norms
+                          * formed across workgroups (the post's section
+                          * "distributed co-design", paper Eq. (8): column
+                          * sums of squares over row shards added up);
+                          * 0: two passes, momentum and column sums first,
+                          * then the weight update (M read twice).  Same
+                          * values up to the order of the sums.             */
+  int32_t reserved0;     /* must be 0                                       */
 } muon_config;
 
 typedef struct muon_ctx muon_ctx;
@@ -172,6 +182,16 @@ muon_status muon_state(const muon_ctx* ctx, int32_t i, int32_t which,
  * refreshes; MuonBP abstract for the block variant). */
 int32_t muon_branch(const muon_config* cfg, int64_t step);
 
+/* Wait for the context's stream, then report what the device recorded.
+ * MUON_E_HIP: the wait failed (a kernel fault or an earlier HIP error).
+ * MUON_E_STATE: in some step since muon_init, a workgroup of the
+ *   single-pass tall RowNorm kernel stopped waiting for its column strip
+ *   after its poll limit (possible only when other work holds most of the
+ *   device's compute units, so that a strip's workgroups cannot all be
+ *   resident); the weights of that step are wrong.  The library never
+ *   waits on the host otherwise; call this where a check is wanted. */
+muon_status muon_sync(muon_ctx* ctx);
+
 /* Release host-side plan memory.  Does not touch the state buffer or the
  * stream; the caller must not free the state buffer while the stream still
  * runs the context's work.  NULL is ignored. */
@@ -198,7 +218,8 @@ typedef enum muon_kernel_class {
   MUON_K_NS_PRODUCT_LAST = 8,/* refresh: last round, fused W update          */
   MUON_K_ADAMW = 9,          /* AdamW on the non-matrix tensors              */
   MUON_K_ROWNORM_COEF = 10,  /* RowNorm step, tall: column coefficients      */
-  MUON_K_COUNT = 11
+  MUON_K_ROWNORM_TALL = 11,  /* RowNorm step, tall, single pass              */
+  MUON_K_COUNT = 12
 } muon_kernel_class;
 
 /* While enabled (enable != 0), muon_step records a HIP event before and

@@ -13,7 +13,7 @@ from .binding import (  # noqa: F401
     EXPORTED, KERNEL_CLASSES, MUON_BF16, MUON_BRANCH_BLOCK_NS5, MUON_BRANCH_NS5, MUON_BRANCH_ROWNORM, MUON_F32,
     MUON_KIND_ADAMW, MUON_KIND_MATRIX, MUON_NS_BF16, MUON_NS_F32, MuonConfig, MuonError,
     MuonTensor, lib, muon_branch, muon_config_default, muon_free, muon_init, muon_last_error,
-    muon_state, muon_state_bytes, muon_status_str, muon_step, muon_timing_enable,
+    muon_state, muon_state_bytes, muon_status_str, muon_step, muon_sync, muon_timing_enable,
     muon_timing_read, tensor_desc)
 
 
@@ -60,6 +60,10 @@ class MuonSession:
         n = v.rows * v.cols
         t = self.state[start:start + 4 * n].view(torch.float32)
         return t.view(v.rows, v.cols) if self.params[i].dim() == 2 else t.view(self.params[i].shape)
+
+    def sync(self) -> None:
+        """Wait for the stream; raises if the device recorded a failed wait."""
+        muon_sync(self.ctx)
 
     def branch(self, t: int) -> int:
         return muon_branch(self.cfg, t)

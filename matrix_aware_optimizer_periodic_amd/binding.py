@@ -23,11 +23,12 @@ MUON_NS_BF16, MUON_NS_F32 = 0, 1
 
 EXPORTED = ("muon_config_default", "muon_state_bytes", "muon_init", "muon_step", "muon_state",
             "muon_branch", "muon_free", "muon_status_str", "muon_last_error",
-            "muon_timing_enable", "muon_timing_read")
+            "muon_timing_enable", "muon_timing_read", "muon_sync")
 
 # muon_kernel_class, in enum order
 KERNEL_CLASSES = ("rownorm_rows", "rownorm_cols1", "rownorm_cols2", "ns_prep", "ns_scale",
-                  "ns_gram", "ns_poly", "ns_product", "ns_product_last", "adamw", "rownorm_coef")
+                  "ns_gram", "ns_poly", "ns_product", "ns_product_last", "adamw", "rownorm_coef",
+                  "rownorm_tall")
 
 
 class MuonTensor(ctypes.Structure):
@@ -45,7 +46,8 @@ class MuonConfig(ctypes.Structure):
                 ("muon_wd", ctypes.c_float), ("adam_lr", ctypes.c_float),
                 ("adam_b1", ctypes.c_float), ("adam_b2", ctypes.c_float),
                 ("adam_eps", ctypes.c_float), ("adam_wd", ctypes.c_float),
-                ("ns_workspace_max", ctypes.c_uint64)]
+                ("ns_workspace_max", ctypes.c_uint64), ("tall_single_pass", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -116,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.muon_timing_enable.restype = ctypes.c_int
         L.muon_timing_read.argtypes = [ctypes.c_void_p, P(ctypes.c_double), P(ctypes.c_int64)]
         L.muon_timing_read.restype = ctypes.c_int
+        L.muon_sync.argtypes = [ctypes.c_void_p]
+        L.muon_sync.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -216,3 +220,8 @@ def muon_timing_read(ctx) -> dict:
     cnt = (ctypes.c_int64 * n)()
     _check(lib().muon_timing_read(ctx, ms, cnt), ctx)
     return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
+
+
+def muon_sync(ctx) -> None:
+    """Wait for the context's stream; raises MuonError on what the device recorded."""
+    _check(lib().muon_sync(ctx), ctx)

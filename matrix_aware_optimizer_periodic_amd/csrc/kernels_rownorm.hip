@@ -391,6 +391,291 @@ __global__ __launch_bounds__(kThreads) void rownorm_coef_kernel(
   d.part[col] = sc.lr * sc.gamma / fmaxf(sqrtf(s), sc.eps_row);
 }
 
+
+// ---- Tall matrices in one pass ------------------------------------------
+//
+// The same column normalisation as above without the second read of M: a
+// workgroup keeps its tile's new momentum in registers while the column
+// sums of squares of the whole strip are formed, then updates W from those
+// registers.  Per element this is G, M and W read once and M, W written
+// once (18 B with bf16 gradients), where the two-pass form re-reads M.
+//
+// Tiles are kTallRows x kTallCols; thread (rg = tid / 64, ct = tid % 64)
+// owns columns c0 + 2ct, c0 + 2ct + 1 and rows rg, rg + 8, ... of the tile.
+// Workgroup b takes tile b, and the tile table lists each strip's row chunks
+// consecutively.  Each workgroup stores its column partials and arrives at
+// the strip; the last to arrive adds the strip's partials in a fixed order
+// (8 waves over consecutive chunk ranges, then a fixed tree), writes
+// lr * gamma / max(||column||, eps) behind the partials and raises the
+// strip's ready word, which the others wait on.  While they wait, their
+// first rows of W are already loading.
+//
+// Why every wait ends: the device deals workgroup ids round-robin to its 8
+// XCDs, and each XCD starts its share in id order.  Take the first strip
+// (by id) still missing an arrival.  Every earlier strip has all arrived, so
+// its workgroups leave; an XCD that has not yet started all of its
+// workgroups of this strip therefore holds no others that stay, and a strip
+// of <= kTallMaxChunks workgroups has at most kTallMaxChunks / 8 on one XCD,
+// which the host checks is at most half of what an XCD holds at once.  So
+// the strip's workgroups all start and arrive, and by induction every strip
+// does.  (Ids claimed at run time from a counter would not do: near the end
+// of a launch the XCD with workgroups left would have to hold whole strips.)
+// A wait still gives up after kTallSpinMax polls and counts that in
+// *giveups, which the host reports.
+//
+// Partials and coefficients cross workgroups, and with them the XCDs'
+// separate L2 caches, within the launch.  Each strip owns padded rows of its
+// own (kTallCols floats: nchunk partial rows, then the coefficient row), so
+// no cache line holds two strips' values, and both sides access them with
+// agent-scope atomic stores and loads, ordered by agent-scope release and
+// acquire fences around the strip's counters.
+// Every counter is back at zero when the launch ends (the reducer resets the
+// arrivals, the last workgroup to leave a strip its ready word and
+// departures), so launches need no clearing between them and replay
+// unchanged from a captured graph.
+constexpr int kTallThreads = 512;
+constexpr int kTallRowsPerThread = kTallRows / (kTallThreads / 64);   // 32
+constexpr int kTallBatch = 8;                                         // rows per load batch
+constexpr uint32_t kTallSpinMax = 1u << 18;   // about 0.5 s of polling
+static_assert(kTallCols == 2 * 64, "two columns per lane");
+
+// Counter words are only touched by agent-scope atomics: adds, exchanges
+// and (for polling) loads.
+__device__ __forceinline__ uint32_t rd_counter(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void set_counter(uint32_t* p, uint32_t v) {
+  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 ld2_agent(const float* p) {
+  GLOBAL float* q = (GLOBAL float*)(p);
+  return make_float2(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st2_agent(float* p, float2 v) {
+  GLOBAL float* q = (GLOBAL float*)(p);
+  __hip_atomic_store(q, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wave's memory operations have completed (vmcnt(0) on
+// gfx950: expcnt and lgkmcnt left at their no-wait maxima).  The values
+// that cross workgroups are only stored and loaded with agent-scope atomics,
+// which complete at the agent's coherence point; waiting for them orders
+// them against the counter atomics without an L2 write-back or invalidate.
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float2 add2(float2 a, float2 b) {
+  return make_float2(a.x + b.x, a.y + b.y);
+}
+__device__ __forceinline__ float2 sum8(const float2 (&r)[kTallThreads / 64][64], int ct) {
+  return add2(add2(add2(r[0][ct], r[1][ct]), add2(r[2][ct], r[3][ct])),
+              add2(add2(r[4][ct], r[5][ct]), add2(r[6][ct], r[7][ct])));
+}
+
+// Rows of a tile are addressed through raw buffer resources based at the
+// tile's first row and sized to its valid rows.  A lane's offset holds only
+// its columns; the row, the same across a wave, is a scalar offset.  Lanes
+// past the last column carry an offset beyond the buffer, so their loads
+// return zeros and their stores are dropped.  Rows past the tile's end are
+// clamped to its last row for loads, and skipped (a wave-uniform branch)
+// for sums and stores.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int64_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(nbytes), 0x00020000);
+}
+__device__ __forceinline__ float2 bld2(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  const f32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_float2(v.x, v.y);
+}
+
+// A store whose data registers the next instructions may reuse, with three
+// wait states after it.  The compiler has left none when a 16-byte store
+// ended a conditional block and the join block began by writing its data
+// registers (a 64-bit move, gfx950): the store's last lanes then took the
+// new values.  These stores are 8 bytes; the guard costs three cycles.
+__device__ __forceinline__ void bst2_guarded(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                             unsigned soff, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(f32x2v{v.x, v.y}, r, voff, soff, 0);
+  asm volatile("s_nop 2" ::: "memory");
+}
+
+// Byte offset of row rg + 8u of the tile (clamped to its last row), es
+// bytes per element; 32-bit scalar arithmetic (a tile buffer is < 2 GiB).
+__device__ __forceinline__ unsigned tall_row(int rg, int u, int rows, unsigned n, unsigned es) {
+  return unsigned(min(rg + 8 * u, rows - 1)) * n * es;
+}
+
+// Momentum update of a thread's rows (row rg + 8u of the tile, columns
+// col, col + 1 at lane offset vcol = 4 col, or past the buffer).  All M
+// loads are issued first, then the gradients in batches of 8 rows, which
+// keeps the kernel within 128 registers (two workgroups per CU).
+template <int GDT>
+__device__ __forceinline__ void tall_momentum(const void* g, __amdgpu_buffer_rsrc_t rm,
+                                              int64_t r0, int rows, unsigned n, unsigned vcol,
+                                              int rg, float beta,
+                                              float2 (&mv)[kTallRowsPerThread]) {
+  constexpr int RPT = kTallRowsPerThread;
+  constexpr unsigned GES = GDT == 1 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rgr =
+      tile_rsrc(static_cast<const char*>(g) + r0 * n * GES, int64_t(rows) * n * GES);
+  const unsigned vg = GDT == 1 ? vcol / 2 : vcol;   // the out-of-range mark stays out of range
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) mv[u] = bld2(rm, vcol, tall_row(rg, u, rows, n, 4));
+#pragma unroll
+  for (int b = 0; b < RPT; b += kTallBatch) {
+    float2 gv[kTallBatch];
+#pragma unroll
+    for (int u = 0; u < kTallBatch; ++u) {
+      const unsigned so = tall_row(rg, b + u, rows, n, GES);
+      if constexpr (GDT == 1) {
+        const unsigned q = __builtin_amdgcn_raw_buffer_load_b32(rgr, vg, so, 0);
+        gv[u] = make_float2(bf16_to_f32(q & 0xffffu), bf16_to_f32(q >> 16));
+      } else {
+        gv[u] = bld2(rgr, vg, so);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTallBatch; ++u)
+      mv[b + u] = make_float2(fmaf(beta, mv[b + u].x, gv[u].x), fmaf(beta, mv[b + u].y, gv[u].y));
+  }
+}
+
+__global__ __launch_bounds__(kTallThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __restrict__ tiles,
+                         TallSync* __restrict__ sync, uint32_t* __restrict__ giveups,
+                         StepScalars sc) {
+  constexpr int RPT = kTallRowsPerThread;
+  constexpr int B = kTallBatch;
+  __shared__ float2 red[kTallThreads / 64][64];
+  __shared__ float2 cf[64];
+  __shared__ uint32_t s_reducer;
+  const int tid = threadIdx.x;
+  const TileItem it = tiles[blockIdx.x];
+  const MatDev d = mats[it.id];
+  TallSync* sy = sync + d.sync0 + it.tj;
+  const int64_t m = d.rows;
+  const unsigned n = unsigned(d.cols);   // tall: n < m <= kTallMaxChunks * kTallRows
+  const uint32_t nchunk = static_cast<uint32_t>((m + kTallRows - 1) / kTallRows);
+  const int64_t r0 = int64_t(it.ti) * kTallRows;
+  const int rows = int(min(m, r0 + kTallRows) - r0);
+  const int rg = __builtin_amdgcn_readfirstlane(tid >> 6), ct = tid & 63;
+  const int64_t col = int64_t(it.tj) * kTallCols + 2 * ct;
+  const bool act = col < n;
+  const unsigned voff = act ? unsigned(col * 4) : 0x80000000u;   // beyond any tile buffer
+  const __amdgpu_buffer_rsrc_t rm = tile_rsrc(d.mom + r0 * n, int64_t(rows) * n * 4);
+  const __amdgpu_buffer_rsrc_t rw = tile_rsrc(d.w + r0 * n, int64_t(rows) * n * 4);
+  // this strip's partial rows 0 .. nchunk - 1, then its coefficient row
+  float* const sp = d.part + int64_t(it.tj) * (nchunk + 1) * kTallCols + 2 * ct;
+
+  // 1. momentum, kept in registers; column sums of squares in row order.
+  float2 mv[RPT];
+  {
+    if (d.gdt == 1) tall_momentum<1>(d.g, rm, r0, rows, n, voff, rg, sc.beta, mv);
+    else tall_momentum<0>(d.g, rm, r0, rows, n, voff, rg, sc.beta, mv);
+    float2 ss = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      if (rg + 8 * u < rows) {
+        const float2 q = mv[u];
+        bst2_guarded(rm, voff, tall_row(rg, u, rows, n, 4), q);
+        ss = make_float2(fmaf(q.x, q.x, ss.x), fmaf(q.y, q.y, ss.y));
+      }
+    }
+    red[rg][ct] = ss;
+  }
+  __syncthreads();
+  // 2. the tile's column partials (wave 0), then arrival at the strip.
+  if (rg == 0) {
+    if (act) st2_agent(sp + int64_t(it.ti) * kTallCols, sum8(red, ct));
+    if (tid == 0) {
+      wait_vmem();   // wave 0's partial stores are complete
+      s_reducer = atomicAdd(&sy->arrive, 1u) == nchunk - 1;
+    }
+  }
+  // the first rows of W load during the wait
+  float2 wv[B];
+#pragma unroll
+  for (int u = 0; u < B; ++u) wv[u] = bld2(rw, voff, tall_row(rg, u, rows, n, 4));
+  __syncthreads();
+  float2 coef;
+  if (__builtin_amdgcn_readfirstlane(s_reducer)) {
+    // 3a. last arrival: every partial of the strip is published.
+    __syncthreads();
+    const uint32_t q = (nchunk + 7) / 8;
+    const uint32_t k0 = min(nchunk, rg * q), k1 = min(nchunk, k0 + q);
+    float2 s = make_float2(0.f, 0.f);
+    for (uint32_t k = k0; k < k1; k += 8) {
+      float2 pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = ld2_agent(sp + int64_t(min(k + u, k1 - 1)) * kTallCols);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k + u < k1) s = add2(s, pv[u]);
+    }
+    __syncthreads();   // red is reused
+    red[rg][ct] = s;
+    __syncthreads();
+    if (rg == 0) {
+      const float2 t = sum8(red, ct);
+      const float lg = sc.lr * sc.gamma;
+      const float2 c = make_float2(lg / fmaxf(sqrtf(t.x), sc.eps_row),
+                                   lg / fmaxf(sqrtf(t.y), sc.eps_row));
+      cf[ct] = c;
+      if (act) st2_agent(sp + int64_t(nchunk) * kTallCols, c);
+      if (tid == 0) {
+        wait_vmem();   // wave 0's coefficient stores are complete
+        set_counter(&sy->arrive, 0u);
+        set_counter(&sy->ready, 1u);
+      }
+    }
+    __syncthreads();
+    coef = cf[ct];
+  } else {
+    // 3b. wait for the strip's coefficients.
+    if (tid == 0) {
+      uint32_t spins = 0;
+      while (rd_counter(&sy->ready) == 0u) {
+        if (++spins > kTallSpinMax) { atomicAdd(giveups, 1u); break; }
+        __builtin_amdgcn_s_sleep(10);   // about 640 clocks between polls
+      }
+    }
+    __syncthreads();
+    coef = ld2_agent(sp + int64_t(nchunk) * kTallCols);
+  }
+  // 4. W <- W (1 - lr wd) - coef M, loads of 8 rows ahead of their stores.
+  const float wkeep = 1.0f - sc.lr * sc.wd;
+#pragma unroll
+  for (int b = 0; b < RPT; b += B) {
+    if (b > 0) {
+#pragma unroll
+      for (int u = 0; u < B; ++u) wv[u] = bld2(rw, voff, tall_row(rg, b + u, rows, n, 4));
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float2 mm = mv[b + u], ww = wv[u];
+      if (rg + 8 * (b + u) < rows)
+        bst2_guarded(rw, voff, tall_row(rg, b + u, rows, n, 4),
+                     make_float2(fmaf(-coef.x, mm.x, ww.x * wkeep),
+                                 fmaf(-coef.y, mm.y, ww.y * wkeep)));
+    }
+  }
+  // 5. leave the strip; the last one out clears it for the next launch.
+  __syncthreads();   // every thread holds its coefficients
+  if (tid == 0) {
+    if (atomicAdd(&sy->depart, 1u) == nchunk - 1) {
+      set_counter(&sy->depart, 0u);
+      set_counter(&sy->ready, 0u);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rownorm_coef(hipStream_t s, const MatDev* mats, const TileItem* strips,
@@ -428,6 +713,20 @@ hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem
   else
     rownorm_cols_kernel<2><<<grid, block, 0, s>>>(mats, tiles, sc);
   return hipGetLastError();
+}
+
+hipError_t launch_rownorm_tall(hipStream_t s, const MatDev* mats, const TileItem* tiles,
+                               int64_t ntiles, TallSync* sync, uint32_t* giveups,
+                               StepScalars sc) {
+  if (ntiles <= 0) return hipSuccess;
+  rownorm_tall_kernel<<<dim3(static_cast<unsigned>(ntiles)), dim3(kTallThreads), 0, s>>>(
+      mats, tiles, sync, giveups, sc);
+  return hipGetLastError();
+}
+
+hipError_t rownorm_tall_resident(int* workgroups_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(workgroups_per_cu, rownorm_tall_kernel,
+                                                      kTallThreads, 0);
 }
 
 }  // namespace muon

@@ -16,9 +16,22 @@ struct MatDev {
   const void* g;     // gradient, same shape (caller-owned), dtype = gdt
   float* mom;        // momentum, rows x cols fp32 (state buffer)
   int64_t rows, cols;
-  float* part;       // RowNorm column partial sums (tall kernel), nchunk x cols
+  float* part;       // RowNorm column partial sums (tall kernels).  Two-pass:
+                     // one row of cols per row chunk.  Single pass: per
+                     // column strip, one row of kTallCols per row chunk,
+                     // then the strip's coefficient row.
   int32_t gdt;       // 0 = f32, 1 = bf16
-  int32_t pad;
+  int32_t sync0;     // single-pass tall RowNorm: first TallSync of this matrix
+};
+
+// Cross-workgroup state of one column strip of the single-pass tall RowNorm
+// kernel, one 128-byte cache line per strip (waiting workgroups poll it).
+// All words are zero between launches.
+struct TallSync {
+  uint32_t arrive;   // workgroups that have published their partials
+  uint32_t depart;   // workgroups done with the coefficients
+  uint32_t ready;    // 1 once the coefficients are published
+  uint32_t pad[29];
 };
 
 // One AdamW tensor (flattened).
@@ -105,6 +118,15 @@ hipError_t launch_rownorm_coef(hipStream_t s, const MatDev* mats, const TileItem
                                int64_t nstrips, StepScalars sc);
 hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem* tiles,
                                int64_t ntiles, int phase, StepScalars sc);
+// Column-normalised (tall) matrices in one pass: tiles kTallRows x
+// kTallCols listed strip by strip (row chunks of a strip consecutive),
+// one workgroup per tile.  *giveups counts waits that gave up (zero unless
+// the residency bound is broken).
+hipError_t launch_rownorm_tall(hipStream_t s, const MatDev* mats, const TileItem* tiles,
+                               int64_t ntiles, TallSync* sync, uint32_t* giveups,
+                               StepScalars sc);
+// Workgroups of the single-pass tall kernel that fit on one CU at once.
+hipError_t rownorm_tall_resident(int* workgroups_per_cu);
 // Refresh prep: momentum, Frobenius partials, unscaled X0 in both layouts.
 hipError_t launch_ns_prep(hipStream_t s, const MatDev* mats, const NsDev* ns,
                           const TileItem* items, int64_t nitems, int prec, float beta);
@@ -124,6 +146,9 @@ constexpr int kGemmProductLast = 3;  // kernel variant only: product that update
 constexpr int kRowChunkElems = 1024;   // elements per row-kernel chunk (256 thr x 4)
 constexpr int kColTileRows = 512;      // tall RowNorm tile rows
 constexpr int kColTileCols = 256;      // tall RowNorm tile columns
+constexpr int kTallRows = 256;         // single-pass tall RowNorm tile rows
+constexpr int kTallCols = 128;         // single-pass tall RowNorm strip width
+constexpr int kTallMaxChunks = 128;    // single pass only for rows <= 128 * 256
 constexpr int kPrepTile = 64;          // NS5 cast/transpose tile
 constexpr int kAdamChunk = 4096;       // elements per AdamW workgroup
 

@@ -67,9 +67,13 @@ struct Plan {
   std::vector<RowGroup> row_groups;
   std::vector<TileItem> col_tiles;
   std::vector<TileItem> col_strips;   // (matrix, 0, column strip) of the tall matrices
+  std::vector<TileItem> tall_tiles;   // single-pass tall tiles, strip by strip
+  int64_t n_col_tiles_max = 0, n_col_strips_max = 0, n_tall_tiles_max = 0, n_tall_sync_max = 0;
+  int32_t n_tall_sync = 0;
   std::vector<AdamChunk> adam_chunks;
   std::vector<NsChunk> ns_full, ns_block;
   size_t off_mats = 0, off_adams = 0, off_col_tiles = 0, off_col_strips = 0, off_adam_chunks = 0;
+  size_t off_tall_tiles = 0, off_tall_sync = 0, tall_sync_bytes = 0;
   size_t ws_base = 0, ws_bytes = 0;
   size_t zero_end = 0;                    // bytes [0, zero_end) are zeroed at init
   size_t total = 0;
@@ -102,6 +106,8 @@ muon_status check_config(const muon_config* c, std::string& err) {
     err = "ns_precision must be MUON_NS_BF16 or MUON_NS_F32"; return MUON_E_ARG;
   }
   if (c->rownorm_axis != 0 && c->rownorm_axis != 1) { err = "rownorm_axis must be 0 or 1"; return MUON_E_ARG; }
+  if (c->tall_single_pass != 0 && c->tall_single_pass != 1) { err = "tall_single_pass must be 0 or 1"; return MUON_E_ARG; }
+  if (c->reserved0 != 0) { err = "reserved0 must be 0"; return MUON_E_ARG; }
   if (c->bp_blocks < 0) { err = "bp_blocks must be >= 0"; return MUON_E_ARG; }
   if (c->bp_blocks > 0 && c->bp_period < 1) { err = "bp_period must be >= 1"; return MUON_E_ARG; }
   if (!(c->adam_b1 >= 0.f && c->adam_b1 < 1.f) || !(c->adam_b2 >= 0.f && c->adam_b2 < 1.f)) {
@@ -278,8 +284,14 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
   return chunks;
 }
 
+// tall_limit: the largest number of row chunks (kTallRows each) a tall
+// matrix may have to take the single-pass RowNorm kernel, set by how many of
+// its workgroups the device holds at once.  Table and buffer sizes are
+// reserved for every eligible matrix either way, so the state size does not
+// depend on it.
 muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const int32_t* kinds,
-                       int32_t n, char* base, Plan& pl, std::string& err) {
+                       int32_t n, char* base, Plan& pl, std::string& err,
+                       int64_t tall_limit = kTallMaxChunks) {
   pl = Plan();
   Bump bump;
   pl.table_index.assign(n, -1);
@@ -315,16 +327,37 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
     const int32_t mi = pl.table_index[i];
     if (cols_mode && t.rows > t.cols) {
       const int64_t nchunk = ceil_div(t.rows, kColTileRows);
-      if (nchunk > 32767 || ceil_div(t.cols, kColTileCols) > 32767) {
+      const int64_t nstrip = ceil_div(t.cols, kColTileCols);
+      if (nchunk > 32767 || nstrip > 32767) {
         err = "param " + std::to_string(i) + ": too large for the tile index range";
         return MUON_E_SHAPE;
       }
-      pl.part_off[i] = bump.take(size_t(nchunk) * t.cols * 4);
-      for (int64_t a = 0; a < nchunk; ++a)
-        for (int64_t b = 0; b < ceil_div(t.cols, kColTileCols); ++b)
-          pl.col_tiles.push_back(TileItem{mi, int16_t(a), int16_t(b)});
-      for (int64_t b = 0; b < ceil_div(t.cols, kColTileCols); ++b)
-        pl.col_strips.push_back(TileItem{mi, 0, int16_t(b)});
+      const int64_t tchunk = ceil_div(t.rows, kTallRows);
+      const int64_t tstrip = ceil_div(t.cols, kTallCols);
+      const bool eligible = cfg.tall_single_pass != 0 && t.cols % 2 == 0 && tchunk <= kTallMaxChunks;
+      // single pass: per strip, tchunk partial rows and a coefficient row of
+      // kTallCols floats each (no cache line shared between strips)
+      pl.part_off[i] = bump.take(std::max(eligible ? size_t(tchunk + 1) * tstrip * kTallCols * 4 : 0,
+                                          size_t(nchunk) * t.cols * 4));
+      pl.n_col_tiles_max += nchunk * nstrip;
+      pl.n_col_strips_max += nstrip;
+      if (eligible) {
+        pl.n_tall_tiles_max += tchunk * tstrip;
+        pl.n_tall_sync_max += tstrip;
+      }
+      if (eligible && tchunk <= tall_limit) {
+        pl.mats[mi].sync0 = pl.n_tall_sync;
+        pl.n_tall_sync += int32_t(tstrip);
+        for (int64_t b = 0; b < tstrip; ++b)
+          for (int64_t a = 0; a < tchunk; ++a)
+            pl.tall_tiles.push_back(TileItem{mi, int16_t(a), int16_t(b)});
+      } else {
+        for (int64_t a = 0; a < nchunk; ++a)
+          for (int64_t b = 0; b < nstrip; ++b)
+            pl.col_tiles.push_back(TileItem{mi, int16_t(a), int16_t(b)});
+        for (int64_t b = 0; b < nstrip; ++b)
+          pl.col_strips.push_back(TileItem{mi, 0, int16_t(b)});
+      }
     } else {
       const int cls = row_chunk_class(t.cols);
       RowGroup& g = groups[std::find(classes, classes + 7, cls) - classes];
@@ -381,8 +414,12 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
   // 5. tables
   pl.off_mats = bump.take(pl.mats.size() * sizeof(MatDev));
   pl.off_adams = bump.take(pl.adams.size() * sizeof(AdamDev));
-  pl.off_col_tiles = bump.take(pl.col_tiles.size() * sizeof(TileItem));
-  pl.off_col_strips = bump.take(pl.col_strips.size() * sizeof(TileItem));
+  pl.off_col_tiles = bump.take(size_t(pl.n_col_tiles_max) * sizeof(TileItem));
+  pl.off_col_strips = bump.take(size_t(pl.n_col_strips_max) * sizeof(TileItem));
+  pl.off_tall_tiles = bump.take(size_t(pl.n_tall_tiles_max) * sizeof(TileItem));
+  // give-up count (word 1 of 16 B), then one TallSync per strip
+  pl.tall_sync_bytes = pl.n_tall_tiles_max ? 16 + size_t(pl.n_tall_sync_max) * sizeof(TallSync) : 0;
+  pl.off_tall_sync = bump.take(pl.tall_sync_bytes);
   pl.off_adam_chunks = bump.take(pl.adam_chunks.size() * sizeof(AdamChunk));
   for (RowGroup& g : pl.row_groups) {
     g.off_ids = bump.take(g.ids.size() * 4);
@@ -607,6 +644,7 @@ muon_status muon_config_default(muon_config* out) {
   out->adam_eps = 1e-8f;
   out->adam_wd = 0.f;
   out->ns_workspace_max = uint64_t(16) << 30;
+  out->tall_single_pass = 1;
   return MUON_OK;
 }
 
@@ -651,7 +689,20 @@ muon_status muon_init(muon_ctx** out, const muon_config* cfg, const muon_tensor*
   ctx->params.assign(params, params + n);
   ctx->grads.assign(grads, grads + n);
   ctx->kinds.assign(kinds, kinds + n);
-  build_plan(*cfg, params, kinds, n, ctx->base, ctx->plan, err);
+  // The single-pass tall RowNorm kernel needs every workgroup of a column
+  // strip resident at once; strips of up to half the device's capacity (so
+  // up to half of each XCD's, as a strip's workgroups are dealt round-robin
+  // to the XCDs) take it, the rest the two-pass kernels.
+  int64_t tall_limit = 0;
+  if (probe.n_tall_tiles_max > 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        rownorm_tall_resident(&per_cu) == hipSuccess)
+      tall_limit = std::min<int64_t>(kTallMaxChunks, int64_t(cus) * per_cu / 2);
+    (void)hipGetLastError();
+  }
+  build_plan(*cfg, params, kinds, n, ctx->base, ctx->plan, err, tall_limit);
   Plan& pl = ctx->plan;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t k = pl.table_index[i];
@@ -678,9 +729,14 @@ muon_status muon_init(muon_ctx** out, const muon_config* cfg, const muon_tensor*
     e = hipMemsetAsync(ctx->base, 0, pl.zero_end, ctx->stream);
     if (e != hipSuccess) return fail(e, "hipMemsetAsync(state)");
   }
+  if (pl.tall_sync_bytes) {
+    e = hipMemsetAsync(ctx->base + pl.off_tall_sync, 0, pl.tall_sync_bytes, ctx->stream);
+    if (e != hipSuccess) return fail(e, "hipMemsetAsync(tall sync)");
+  }
   const hipError_t ups[] = {
       upload(ctx, pl.off_mats, pl.mats), upload(ctx, pl.off_adams, pl.adams),
       upload(ctx, pl.off_col_tiles, pl.col_tiles), upload(ctx, pl.off_col_strips, pl.col_strips),
+      upload(ctx, pl.off_tall_tiles, pl.tall_tiles),
       upload(ctx, pl.off_adam_chunks, pl.adam_chunks)};
   for (hipError_t u : ups)
     if (u != hipSuccess) return fail(u, "hipMemcpyAsync(tables)");
@@ -773,6 +829,13 @@ muon_status muon_step(muon_ctx* ctx, const muon_tensor* params, const muon_tenso
             g.prefix.back(), g.max_chunks, sc));
         if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_rows"); }
       }
+      if (!pl.tall_tiles.empty()) {
+        uint32_t* ctl = reinterpret_cast<uint32_t*>(ctx->base + pl.off_tall_sync);
+        const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_TALL, launch_rownorm_tall(
+            ctx->stream, mats, reinterpret_cast<const TileItem*>(ctx->base + pl.off_tall_tiles),
+            int64_t(pl.tall_tiles.size()), reinterpret_cast<TallSync*>(ctl + 4), ctl + 1, sc));
+        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_tall"); }
+      }
       const TileItem* tiles = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_tiles);
       const TileItem* strips = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_strips);
       for (int phase = 1; phase <= 2 && !pl.col_tiles.empty(); ++phase) {
@@ -857,6 +920,24 @@ muon_status muon_timing_read(muon_ctx* ctx, double* ms, int64_t* launches) {
   for (int k = 0; k < MUON_K_COUNT; ++k) {
     if (ms) ms[k] = acc[k];
     if (launches) launches[k] = cnt[k];
+  }
+  return MUON_OK;
+}
+
+muon_status muon_sync(muon_ctx* ctx) {
+  if (!ctx) return MUON_E_ARG;
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "muon_sync"); }
+  const Plan& pl = ctx->plan;
+  if (pl.tall_sync_bytes) {
+    uint32_t ctl[2] = {0, 0};
+    e = hipMemcpy(ctl, ctx->base + pl.off_tall_sync, sizeof ctl, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "muon_sync"); }
+    if (ctl[1] != 0) {
+      ctx->err = std::to_string(ctl[1]) +
+                 " single-pass tall RowNorm workgroup(s) stopped waiting for their column strip";
+      return MUON_E_STATE;
+    }
   }
   return MUON_OK;
 }
