@@ -193,6 +193,26 @@ def test_tall_rownorm_single_and_two_pass(single, grad_dtype):
         sess.close()
 
 
+def test_tall_single_pass_with_two_pass_fallback():
+    """One context holding tall matrices the single pass takes (1000 x 300)
+    and ones it leaves to the two-pass kernels: more than 32768 rows
+    (33000 x 40) and an odd column count (700 x 301).  Both kernel families
+    run in the same RowNorm step, and every matrix matches the oracle."""
+    m = _lib()
+    shapes = [(33000, 40), (700, 301), (1000, 300)]
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    G = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    sess = m.MuonSession(W, G, kinds=[m.MUON_KIND_MATRIX] * len(shapes))
+    try:
+        m.muon_timing_enable(sess.ctx, True)
+        _direction_loop(sess, shapes, 3, W, G, torch.bfloat16, "bf16", 1e-3, 5, None)
+        sess.sync()
+        rec = m.muon_timing_read(sess.ctx)
+        assert rec["rownorm_tall"][1] == 2 and rec["rownorm_cols1"][1] == 2
+    finally:
+        sess.close()
+
+
 def test_tall_single_pass_repeated_launches():
     """Twenty RowNorm steps in a row on a set of tall matrices (DiT-1.3B
     qkv, adaLN and fc1 shapes among them): the strip counters return to zero
