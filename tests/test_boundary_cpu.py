@@ -57,6 +57,25 @@ def test_defaults_match_the_pages_and_the_oracle():
               "adam_b2", "adam_eps", "bp_lr_ratio"):
         assert abs(getattr(c, f) - getattr(o, f)) <= 1e-6 * max(1.0, abs(getattr(o, f))), f
     assert c.ns_iters == o.ns_iters and c.bp_period == o.bp_period
+    assert c.tall_single_pass == 1 and c.reserved0 == 0
+
+
+def test_state_bytes_do_not_depend_on_the_tall_rownorm_form():
+    """The state buffer holds the tables and partial sums of both tall
+    RowNorm forms (the device decides at init which matrices take the single
+    pass), so its size is a host-only function of the shapes: the same with
+    the single pass on or off, and larger than the two-pass form alone would
+    need for tall matrices whose single-pass partials take more room."""
+    wl = workloads.WORKLOADS["dit-1.3b"]
+    ps = [desc(a, b) for _, a, b in wl.shapes]
+    on = m.muon_state_bytes(m.muon_config_default(), ps, [0] * len(ps))
+    off = m.muon_state_bytes(m.muon_config_default(tall_single_pass=0), ps, [0] * len(ps))
+    assert on >= off
+    # wide matrices and tall ones the single pass cannot take size the same either way
+    for shape in [(2048, 8192), (700, 301), (33000, 40)]:
+        a = m.muon_state_bytes(m.muon_config_default(), [desc(*shape)], [0])
+        b = m.muon_state_bytes(m.muon_config_default(tall_single_pass=0), [desc(*shape)], [0])
+        assert a == b, shape
 
 
 @pytest.mark.parametrize("K", [1, 2, 3, 4, 7])
@@ -117,7 +136,8 @@ def test_state_bytes_rejects_bad_params(bad, status):
 @pytest.mark.parametrize("field,value", [("K", 0), ("ns_iters", 0), ("ns_precision", 3),
                                          ("rownorm_axis", 2), ("bp_blocks", -1),
                                          ("adam_b1", 1.0), ("eps_row", -1.0),
-                                         ("lr", float("nan"))])
+                                         ("lr", float("nan")), ("tall_single_pass", 2),
+                                         ("reserved0", 1)])
 def test_config_validation(field, value):
     c = m.muon_config_default(**{field: value})
     with pytest.raises(m.MuonError) as e:
