@@ -285,6 +285,9 @@ def main() -> int:
     wall = time.perf_counter() - t_wall
     step_ms = [starts[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
     total_ms = sum(step_ms)
+    # Raises if a cross-workgroup wait of the single-pass tall RowNorm kernel
+    # gave up in any step so far (those steps' weights would be wrong).
+    sess.sync()
 
     # Per-kernel durations: the same steps again (same branch sequence, K | t0),
     # with the library's own HIP event pairs around every launch on its stream.
@@ -305,6 +308,7 @@ def main() -> int:
                 a = acc.get(name, (0.0, 0))
                 acc[name] = (a[0] + ms, a[1] + cnt)
         mm.muon_timing_enable(sess.ctx, False)
+        sess.sync()
         for acc in kt_branch.values():
             for name, (ms, cnt) in acc.items():
                 a = kt.get(name, (0.0, 0))
