@@ -574,7 +574,8 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
   // this strip's partial rows 0 .. nchunk - 1, then its coefficient row
   float* const sp = d.part + int64_t(it.tj) * (nchunk + 1) * kTallCols + 2 * ct;
 
-  // 1. momentum, kept in registers; column sums of squares in row order.
+  // 1. momentum, kept in registers; column sums of squares in row order
+  //    (the new momentum is stored in step 2).
   float2 mv[RPT];
   {
     if (d.gdt == 1) tall_momentum<1>(d.g, rm, r0, rows, n, voff, rg, sc.beta, mv);
@@ -584,7 +585,6 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
     for (int u = 0; u < RPT; ++u) {
       if (rg + 8 * u < rows) {
         const float2 q = mv[u];
-        bst2_guarded(rm, voff, tall_row(rg, u, rows, n, 4), q);
         ss = make_float2(fmaf(q.x, q.x, ss.x), fmaf(q.y, q.y, ss.y));
       }
     }
@@ -599,10 +599,15 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
       s_reducer = atomicAdd(&sy->arrive, 1u) == nchunk - 1;
     }
   }
-  // the first rows of W load during the wait
+  // the first rows of W load during the wait, then the new momentum is
+  // stored (after those loads: measured 1-2% faster than storing it before
+  // the arrival)
   float2 wv[B];
 #pragma unroll
   for (int u = 0; u < B; ++u) wv[u] = bld2(rw, voff, tall_row(rg, u, rows, n, 4));
+#pragma unroll
+  for (int u = 0; u < RPT; ++u)
+    if (rg + 8 * u < rows) bst2_guarded(rm, voff, tall_row(rg, u, rows, n, 4), mv[u]);
   __syncthreads();
   float2 coef;
   if (__builtin_amdgcn_readfirstlane(s_reducer)) {
