@@ -427,8 +427,11 @@ __global__ __launch_bounds__(kThreads) void rownorm_coef_kernel(
 // separate L2 caches, within the launch.  Each strip owns padded rows of its
 // own (kTallCols floats: nchunk partial rows, then the coefficient row), so
 // no cache line holds two strips' values, and both sides access them with
-// agent-scope atomic stores and loads, ordered by agent-scope release and
-// acquire fences around the strip's counters.
+// agent-scope atomic stores and loads.  A writer waits until its wave's
+// stores have completed before touching the strip's counter, and a reader
+// loads them only after the counter it polled has changed; no L2 write-back
+// or invalidate is needed (agent-scope fences, which do both, cost more than
+// the second pass this kernel saves).
 // Every counter is back at zero when the launch ends (the reducer resets the
 // arrivals, the last workgroup to leave a strip its ready word and
 // departures), so launches need no clearing between them and replay
