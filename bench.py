@@ -109,14 +109,14 @@ def measured_traffic(kernel: str, workload: str):
 def rownorm_class_bytes(shapes, gbytes, single_pass=True):
     """Algorithmic bytes per RowNorm step per kernel class (long-axis mode).
 
-    Tall matrices with n a multiple of 4 and at most 32768 rows take the single-pass
+    Tall matrices with even n and at most 32768 rows take the single-pass
     kernel when it is enabled (read G, M, W; write M, W), the others the two
     passes (G, M -> M, then M, W -> W)."""
     rows = cols1 = cols2 = tall = 0
     for m, n in shapes:
         e = m * n
         if m > n:
-            if single_pass and n % 4 == 0 and m <= 32768:
+            if single_pass and n % 2 == 0 and m <= 32768:
                 tall += (gbytes + 16) * e
             else:
                 cols1 += (gbytes + 8) * e      # read G, M; write M

@@ -125,7 +125,7 @@ typedef struct muon_config {
                          /* (1e-3, 0.9, 0.999, 1e-8, 0)                     */
   uint64_t ns_workspace_max; /* cap on NS5 workspace bytes; 0 = no cap     */
   int32_t tall_single_pass; /* 1 (default): long-axis RowNorm of a tall
-                          * matrix (m > n, n % 4 == 0, m <= 32768) runs as
+                          * matrix (m > n, n even, m <= 32768) runs as
                           * one pass over its tensors, with the column norms
                           * formed across workgroups (the post's section
                           * "distributed co-design", paper Eq. (8): column

@@ -400,15 +400,12 @@ __global__ __launch_bounds__(kThreads) void rownorm_coef_kernel(
 // registers.  Per element this is G, M and W read once and M, W written
 // once (18 B with bf16 gradients), where the two-pass form re-reads M.
 //
-// Tiles are kTallRows x kTallCols (128 x 256); thread (rg = tid / 64,
-// ct = tid % 64) owns columns c0 + 4ct .. c0 + 4ct + 3 (16-byte accesses)
-// and rows rg, rg + 8, ... of the tile.  Two 8-wave workgroups share a CU,
-// so one streams while the other waits at its strip (one 16-wave workgroup
-// per CU on 256 x 256 tiles measured 12% slower).
+// Tiles are kTallRows x kTallCols; thread (rg = tid / 64, ct = tid % 64)
+// owns columns c0 + 2ct, c0 + 2ct + 1 and rows rg, rg + 8, ... of the tile.
 // Workgroup b takes tile b, and the tile table lists each strip's row chunks
 // consecutively.  Each workgroup stores its column partials and arrives at
 // the strip; the last to arrive adds the strip's partials in a fixed order
-// (8 waves over consecutive chunk ranges, then in wave order), writes
+// (8 waves over consecutive chunk ranges, then a fixed tree), writes
 // lr * gamma / max(||column||, eps) behind the partials and raises the
 // strip's ready word, which the others wait on.  While they wait, their
 // first rows of W are already loading.
@@ -440,12 +437,10 @@ __global__ __launch_bounds__(kThreads) void rownorm_coef_kernel(
 // departures), so launches need no clearing between them and replay
 // unchanged from a captured graph.
 constexpr int kTallThreads = 512;
-constexpr int kTallWaves = kTallThreads / 64;                         // 8
-constexpr int kTallRowsPerThread = kTallRows / kTallWaves;            // 16
-constexpr int kTallBatch = 4;                                         // rows per load batch
+constexpr int kTallRowsPerThread = kTallRows / (kTallThreads / 64);   // 32
+constexpr int kTallBatch = 8;                                         // rows per load batch
 constexpr uint32_t kTallSpinMax = 1u << 18;   // about 0.5 s of polling
-static_assert(kTallCols == 4 * 64, "four columns per lane");
-static_assert(kTallRowsPerThread % kTallBatch == 0, "whole load batches");
+static_assert(kTallCols == 2 * 64, "two columns per lane");
 
 // Counter words are only touched by agent-scope atomics: adds, exchanges
 // and (for polling) loads.
@@ -456,19 +451,15 @@ __device__ __forceinline__ void set_counter(uint32_t* p, uint32_t v) {
   (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float4 ld4_agent(const float* p) {
+__device__ __forceinline__ float2 ld2_agent(const float* p) {
   GLOBAL float* q = (GLOBAL float*)(p);
-  return make_float4(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                     __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                     __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                     __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return make_float2(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
-__device__ __forceinline__ void st4_agent(float* p, float4 v) {
+__device__ __forceinline__ void st2_agent(float* p, float2 v) {
   GLOBAL float* q = (GLOBAL float*)(p);
   __hip_atomic_store(q, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(q + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until this wave's memory operations have completed (vmcnt(0) on
@@ -482,16 +473,12 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float4 add4(float4 a, float4 b) {
-  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+__device__ __forceinline__ float2 add2(float2 a, float2 b) {
+  return make_float2(a.x + b.x, a.y + b.y);
 }
-// Sum over the waves' rows of red in wave order (the same order every
-// launch; a running sum keeps the registers of the rows held meanwhile).
-__device__ __forceinline__ float4 sum_waves(const float4 (&r)[kTallWaves][64], int ct) {
-  float4 s = r[0][ct];
-#pragma unroll
-  for (int k = 1; k < kTallWaves; ++k) s = add4(s, r[k][ct]);
-  return s;
+__device__ __forceinline__ float2 sum8(const float2 (&r)[kTallThreads / 64][64], int ct) {
+  return add2(add2(add2(r[0][ct], r[1][ct]), add2(r[2][ct], r[3][ct])),
+              add2(add2(r[4][ct], r[5][ct]), add2(r[6][ct], r[7][ct])));
 }
 
 // Rows of a tile are addressed through raw buffer resources based at the
@@ -501,67 +488,65 @@ __device__ __forceinline__ float4 sum_waves(const float4 (&r)[kTallWaves][64], i
 // return zeros and their stores are dropped.  Rows past the tile's end are
 // clamped to its last row for loads, and skipped (a wave-uniform branch)
 // for sums and stores.
-typedef float f32x4b __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2b __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int64_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(nbytes), 0x00020000);
 }
-__device__ __forceinline__ float4 bld4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-  const f32x4b v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_float4(v.x, v.y, v.z, v.w);
+__device__ __forceinline__ float2 bld2(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  const f32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_float2(v.x, v.y);
 }
 
 // A store whose data registers the next instructions may reuse, with three
 // wait states after it.  The compiler has left none when a 16-byte store
 // ended a conditional block and the join block began by writing its data
 // registers (a 64-bit move, gfx950): the store's last lanes then took the
-// new values.  The guard costs three cycles per store.
-__device__ __forceinline__ void bst4_guarded(__amdgpu_buffer_rsrc_t r, unsigned voff,
-                                             unsigned soff, float4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(f32x4b{v.x, v.y, v.z, v.w}, r, voff, soff, 0);
+// new values.  These stores are 8 bytes; the guard costs three cycles.
+__device__ __forceinline__ void bst2_guarded(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                             unsigned soff, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(f32x2v{v.x, v.y}, r, voff, soff, 0);
   asm volatile("s_nop 2" ::: "memory");
 }
 
-// Byte offset of row rg + kTallWaves u of the tile (clamped to its last
-// row), es bytes per element; 32-bit scalar arithmetic (a tile buffer is
-// < 2 GiB).
+// Byte offset of row rg + 8u of the tile (clamped to its last row), es
+// bytes per element; 32-bit scalar arithmetic (a tile buffer is < 2 GiB).
 __device__ __forceinline__ unsigned tall_row(int rg, int u, int rows, unsigned n, unsigned es) {
-  return unsigned(min(rg + kTallWaves * u, rows - 1)) * n * es;
+  return unsigned(min(rg + 8 * u, rows - 1)) * n * es;
 }
 
 // Momentum update of a thread's rows (row rg + 8u of the tile, columns
-// col .. col + 3 at lane offset vcol = 4 col, or past the buffer).  All M
-// loads are issued first, then the gradients in batches of 4 rows, which
+// col, col + 1 at lane offset vcol = 4 col, or past the buffer).  All M
+// loads are issued first, then the gradients in batches of 8 rows, which
 // keeps the kernel within 128 registers (two workgroups per CU).
 template <int GDT>
 __device__ __forceinline__ void tall_momentum(const void* g, __amdgpu_buffer_rsrc_t rm,
                                               int64_t r0, int rows, unsigned n, unsigned vcol,
                                               int rg, float beta,
-                                              float4 (&mv)[kTallRowsPerThread]) {
+                                              float2 (&mv)[kTallRowsPerThread]) {
   constexpr int RPT = kTallRowsPerThread;
   constexpr unsigned GES = GDT == 1 ? 2 : 4;
   const __amdgpu_buffer_rsrc_t rgr =
       tile_rsrc(static_cast<const char*>(g) + r0 * n * GES, int64_t(rows) * n * GES);
   const unsigned vg = GDT == 1 ? vcol / 2 : vcol;   // the out-of-range mark stays out of range
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) mv[u] = bld4(rm, vcol, tall_row(rg, u, rows, n, 4));
+  for (int u = 0; u < RPT; ++u) mv[u] = bld2(rm, vcol, tall_row(rg, u, rows, n, 4));
 #pragma unroll
   for (int b = 0; b < RPT; b += kTallBatch) {
-    float4 gv[kTallBatch];
+    float2 gv[kTallBatch];
 #pragma unroll
     for (int u = 0; u < kTallBatch; ++u) {
       const unsigned so = tall_row(rg, b + u, rows, n, GES);
       if constexpr (GDT == 1) {
-        const u32x2b q = __builtin_amdgcn_raw_buffer_load_b64(rgr, vg, so, 0);
-        gv[u] = make_float4(bf16_to_f32(q.x & 0xffffu), bf16_to_f32(q.x >> 16),
-                            bf16_to_f32(q.y & 0xffffu), bf16_to_f32(q.y >> 16));
+        const unsigned q = __builtin_amdgcn_raw_buffer_load_b32(rgr, vg, so, 0);
+        gv[u] = make_float2(bf16_to_f32(q & 0xffffu), bf16_to_f32(q >> 16));
       } else {
-        gv[u] = bld4(rgr, vg, so);
+        gv[u] = bld2(rgr, vg, so);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kTallBatch; ++u) mv[b + u] = fma4(beta, mv[b + u], gv[u]);
+    for (int u = 0; u < kTallBatch; ++u)
+      mv[b + u] = make_float2(fmaf(beta, mv[b + u].x, gv[u].x), fmaf(beta, mv[b + u].y, gv[u].y));
   }
 }
 
@@ -571,41 +556,39 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
                          StepScalars sc) {
   constexpr int RPT = kTallRowsPerThread;
   constexpr int B = kTallBatch;
-  constexpr int NW = kTallWaves;
-  __shared__ float4 red[NW][64];
-  __shared__ float4 cf[64];
+  __shared__ float2 red[kTallThreads / 64][64];
+  __shared__ float2 cf[64];
   __shared__ uint32_t s_reducer;
   const int tid = threadIdx.x;
   const TileItem it = tiles[blockIdx.x];
   const MatDev d = mats[it.id];
   TallSync* sy = sync + d.sync0 + it.tj;
   const int64_t m = d.rows;
-  const unsigned n = unsigned(d.cols);   // tall: n < m <= kTallMaxChunks * kTallRows, n % 4 == 0
+  const unsigned n = unsigned(d.cols);   // tall: n < m <= kTallMaxChunks * kTallRows
   const uint32_t nchunk = static_cast<uint32_t>((m + kTallRows - 1) / kTallRows);
   const int64_t r0 = int64_t(it.ti) * kTallRows;
   const int rows = int(min(m, r0 + kTallRows) - r0);
   const int rg = __builtin_amdgcn_readfirstlane(tid >> 6), ct = tid & 63;
-  const int64_t col = int64_t(it.tj) * kTallCols + 4 * ct;
-  const bool act = col < n;              // all four columns, or none (n % 4 == 0)
+  const int64_t col = int64_t(it.tj) * kTallCols + 2 * ct;
+  const bool act = col < n;
   const unsigned voff = act ? unsigned(col * 4) : 0x80000000u;   // beyond any tile buffer
   const __amdgpu_buffer_rsrc_t rm = tile_rsrc(d.mom + r0 * n, int64_t(rows) * n * 4);
   const __amdgpu_buffer_rsrc_t rw = tile_rsrc(d.w + r0 * n, int64_t(rows) * n * 4);
   // this strip's partial rows 0 .. nchunk - 1, then its coefficient row
-  float* const sp = d.part + int64_t(it.tj) * (nchunk + 1) * kTallCols + 4 * ct;
+  float* const sp = d.part + int64_t(it.tj) * (nchunk + 1) * kTallCols + 2 * ct;
 
   // 1. momentum, kept in registers; column sums of squares in row order
   //    (the new momentum is stored in step 2).
-  float4 mv[RPT];
+  float2 mv[RPT];
   {
     if (d.gdt == 1) tall_momentum<1>(d.g, rm, r0, rows, n, voff, rg, sc.beta, mv);
     else tall_momentum<0>(d.g, rm, r0, rows, n, voff, rg, sc.beta, mv);
-    float4 ss = make_float4(0.f, 0.f, 0.f, 0.f);
+    float2 ss = make_float2(0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
-      if (rg + NW * u < rows) {
-        const float4 q = mv[u];
-        ss = make_float4(fmaf(q.x, q.x, ss.x), fmaf(q.y, q.y, ss.y), fmaf(q.z, q.z, ss.z),
-                         fmaf(q.w, q.w, ss.w));
+      if (rg + 8 * u < rows) {
+        const float2 q = mv[u];
+        ss = make_float2(fmaf(q.x, q.x, ss.x), fmaf(q.y, q.y, ss.y));
       }
     }
     red[rg][ct] = ss;
@@ -613,7 +596,7 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
   __syncthreads();
   // 2. the tile's column partials (wave 0), then arrival at the strip.
   if (rg == 0) {
-    if (act) st4_agent(sp + int64_t(it.ti) * kTallCols, sum_waves(red, ct));
+    if (act) st2_agent(sp + int64_t(it.ti) * kTallCols, sum8(red, ct));
     if (tid == 0) {
       wait_vmem();   // wave 0's partial stores are complete
       s_reducer = atomicAdd(&sy->arrive, 1u) == nchunk - 1;
@@ -622,40 +605,38 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
   // the first rows of W load during the wait, then the new momentum is
   // stored (after those loads: measured 1-2% faster than storing it before
   // the arrival)
-  float4 wv[B];
+  float2 wv[B];
 #pragma unroll
-  for (int u = 0; u < B; ++u) wv[u] = bld4(rw, voff, tall_row(rg, u, rows, n, 4));
+  for (int u = 0; u < B; ++u) wv[u] = bld2(rw, voff, tall_row(rg, u, rows, n, 4));
 #pragma unroll
   for (int u = 0; u < RPT; ++u)
-    if (rg + NW * u < rows) bst4_guarded(rm, voff, tall_row(rg, u, rows, n, 4), mv[u]);
+    if (rg + 8 * u < rows) bst2_guarded(rm, voff, tall_row(rg, u, rows, n, 4), mv[u]);
   __syncthreads();
-  float4 coef;
+  float2 coef;
   if (__builtin_amdgcn_readfirstlane(s_reducer)) {
     // 3a. last arrival: every partial of the strip is published.
     __syncthreads();
-    const uint32_t q = (nchunk + NW - 1) / NW;
+    const uint32_t q = (nchunk + 7) / 8;
     const uint32_t k0 = min(nchunk, rg * q), k1 = min(nchunk, k0 + q);
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (uint32_t k = k0; k < k1; k += 4) {
-      float4 pv[4];
+    float2 s = make_float2(0.f, 0.f);
+    for (uint32_t k = k0; k < k1; k += 8) {
+      float2 pv[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pv[u] = ld4_agent(sp + int64_t(min(k + u, k1 - 1)) * kTallCols);
+      for (int u = 0; u < 8; ++u) pv[u] = ld2_agent(sp + int64_t(min(k + u, k1 - 1)) * kTallCols);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (k + u < k1) s = add4(s, pv[u]);
+      for (int u = 0; u < 8; ++u)
+        if (k + u < k1) s = add2(s, pv[u]);
     }
     __syncthreads();   // red is reused
     red[rg][ct] = s;
     __syncthreads();
     if (rg == 0) {
-      const float4 t = sum_waves(red, ct);
+      const float2 t = sum8(red, ct);
       const float lg = sc.lr * sc.gamma;
-      const float4 c = make_float4(lg / fmaxf(sqrtf(t.x), sc.eps_row),
-                                   lg / fmaxf(sqrtf(t.y), sc.eps_row),
-                                   lg / fmaxf(sqrtf(t.z), sc.eps_row),
-                                   lg / fmaxf(sqrtf(t.w), sc.eps_row));
+      const float2 c = make_float2(lg / fmaxf(sqrtf(t.x), sc.eps_row),
+                                   lg / fmaxf(sqrtf(t.y), sc.eps_row));
       cf[ct] = c;
-      if (act) st4_agent(sp + int64_t(nchunk) * kTallCols, c);
+      if (act) st2_agent(sp + int64_t(nchunk) * kTallCols, c);
       if (tid == 0) {
         wait_vmem();   // wave 0's coefficient stores are complete
         set_counter(&sy->arrive, 0u);
@@ -674,25 +655,23 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
       }
     }
     __syncthreads();
-    coef = act ? ld4_agent(sp + int64_t(nchunk) * kTallCols) : make_float4(0.f, 0.f, 0.f, 0.f);
+    coef = ld2_agent(sp + int64_t(nchunk) * kTallCols);
   }
-  // 4. W <- W (1 - lr wd) - coef M, loads of 4 rows ahead of their stores.
+  // 4. W <- W (1 - lr wd) - coef M, loads of 8 rows ahead of their stores.
   const float wkeep = 1.0f - sc.lr * sc.wd;
 #pragma unroll
   for (int b = 0; b < RPT; b += B) {
     if (b > 0) {
 #pragma unroll
-      for (int u = 0; u < B; ++u) wv[u] = bld4(rw, voff, tall_row(rg, b + u, rows, n, 4));
+      for (int u = 0; u < B; ++u) wv[u] = bld2(rw, voff, tall_row(rg, b + u, rows, n, 4));
     }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      const float4 mm = mv[b + u], ww = wv[u];
-      if (rg + NW * (b + u) < rows)
-        bst4_guarded(rw, voff, tall_row(rg, b + u, rows, n, 4),
-                     make_float4(fmaf(-coef.x, mm.x, ww.x * wkeep),
-                                 fmaf(-coef.y, mm.y, ww.y * wkeep),
-                                 fmaf(-coef.z, mm.z, ww.z * wkeep),
-                                 fmaf(-coef.w, mm.w, ww.w * wkeep)));
+      const float2 mm = mv[b + u], ww = wv[u];
+      if (rg + 8 * (b + u) < rows)
+        bst2_guarded(rw, voff, tall_row(rg, b + u, rows, n, 4),
+                     make_float2(fmaf(-coef.x, mm.x, ww.x * wkeep),
+                                 fmaf(-coef.y, mm.y, ww.y * wkeep)));
     }
   }
   // 5. leave the strip; the last one out clears it for the next launch.

@@ -146,9 +146,9 @@ constexpr int kGemmProductLast = 3;  // kernel variant only: product that update
 constexpr int kRowChunkElems = 1024;   // elements per row-kernel chunk (256 thr x 4)
 constexpr int kColTileRows = 512;      // tall RowNorm tile rows
 constexpr int kColTileCols = 256;      // tall RowNorm tile columns
-constexpr int kTallRows = 128;         // single-pass tall RowNorm tile rows
-constexpr int kTallCols = 256;         // single-pass tall RowNorm strip width
-constexpr int kTallMaxChunks = 256;    // single pass only for rows <= 256 * 128
+constexpr int kTallRows = 256;         // single-pass tall RowNorm tile rows
+constexpr int kTallCols = 128;         // single-pass tall RowNorm strip width
+constexpr int kTallMaxChunks = 128;    // single pass only for rows <= 128 * 256
 constexpr int kPrepTile = 64;          // NS5 cast/transpose tile
 constexpr int kAdamChunk = 4096;       // elements per AdamW workgroup
 

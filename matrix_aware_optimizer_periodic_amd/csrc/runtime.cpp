@@ -334,7 +334,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
       }
       const int64_t tchunk = ceil_div(t.rows, kTallRows);
       const int64_t tstrip = ceil_div(t.cols, kTallCols);
-      const bool eligible = cfg.tall_single_pass != 0 && t.cols % 4 == 0 && tchunk <= kTallMaxChunks;
+      const bool eligible = cfg.tall_single_pass != 0 && t.cols % 2 == 0 && tchunk <= kTallMaxChunks;
       // single pass: per strip, tchunk partial rows and a coefficient row of
       // kTallCols floats each (no cache line shared between strips)
       pl.part_off[i] = bump.take(std::max(eligible ? size_t(tchunk + 1) * tstrip * kTallCols * 4 : 0,

@@ -72,7 +72,7 @@ def test_state_bytes_do_not_depend_on_the_tall_rownorm_form():
     off = m.muon_state_bytes(m.muon_config_default(tall_single_pass=0), ps, [0] * len(ps))
     assert on >= off
     # wide matrices and tall ones the single pass cannot take size the same either way
-    for shape in [(2048, 8192), (700, 301), (900, 302), (33000, 40)]:
+    for shape in [(2048, 8192), (700, 301), (33000, 40)]:
         a = m.muon_state_bytes(m.muon_config_default(), [desc(*shape)], [0])
         b = m.muon_state_bytes(m.muon_config_default(tall_single_pass=0), [desc(*shape)], [0])
         assert a == b, shape

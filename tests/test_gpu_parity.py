@@ -196,11 +196,10 @@ def test_tall_rownorm_single_and_two_pass(single, grad_dtype):
 def test_tall_single_pass_with_two_pass_fallback():
     """One context holding tall matrices the single pass takes (1000 x 300)
     and ones it leaves to the two-pass kernels: more than 32768 rows
-    (33000 x 40) and column counts that are not a multiple of 4 (700 x 301,
-    900 x 302).  Both kernel families run in the same RowNorm step, and every
-    matrix matches the oracle."""
+    (33000 x 40) and an odd column count (700 x 301).  Both kernel families
+    run in the same RowNorm step, and every matrix matches the oracle."""
     m = _lib()
-    shapes = [(33000, 40), (700, 301), (900, 302), (1000, 300)]
+    shapes = [(33000, 40), (700, 301), (1000, 300)]
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     G = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
     sess = m.MuonSession(W, G, kinds=[m.MUON_KIND_MATRIX] * len(shapes))
