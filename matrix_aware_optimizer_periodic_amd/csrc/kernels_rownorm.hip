@@ -401,7 +401,13 @@ __global__ __launch_bounds__(kThreads) void rownorm_coef_kernel(
 // once (18 B with bf16 gradients), where the two-pass form re-reads M.
 //
 // Tiles are kTallRows x kTallCols; thread (rg = tid / 64, ct = tid % 64)
-// owns columns c0 + 2ct, c0 + 2ct + 1 and rows rg, rg + 8, ... of the tile.
+// owns two adjacent columns of the strip and rows rg, rg + 8, ... of the
+// tile.  A strip's 128 columns are four runs of 32, 512 columns apart, so
+// that the rows of one tile, a power-of-two pitch apart in DiT shapes
+// (n = 2048: 8 KB), do not all fall in the same few DRAM channels:
+// contiguous strips streamed about 10% slower at 8 KB and 16 KB pitches than
+// at their neighbours, and runs a quarter of the row apart are 4 KB apart at
+// n = 4096, which lost again.
 // Workgroup b takes tile b, and the tile table lists each strip's row chunks
 // consecutively.  Each workgroup stores its column partials and arrives at
 // the strip; the last to arrive adds the strip's partials in a fixed order
@@ -441,6 +447,8 @@ constexpr int kTallRowsPerThread = kTallRows / (kTallThreads / 64);   // 32
 constexpr int kTallBatch = 8;                                         // rows per load batch
 constexpr uint32_t kTallSpinMax = 1u << 18;   // about 0.5 s of polling
 static_assert(kTallCols == 2 * 64, "two columns per lane");
+constexpr unsigned kTallRunGap = 512;   // columns between a strip's runs
+static_assert(kTallRunGap % 32 == 0, "whole runs");
 
 // Counter words are only touched by agent-scope atomics: adds, exchanges
 // and (for polling) loads.
@@ -569,7 +577,20 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
   const int64_t r0 = int64_t(it.ti) * kTallRows;
   const int rows = int(min(m, r0 + kTallRows) - r0);
   const int rg = __builtin_amdgcn_readfirstlane(tid >> 6), ct = tid & 63;
-  const int64_t col = int64_t(it.tj) * kTallCols + 2 * ct;
+  // Columns of strip tj: four runs of 32 (one per group of 16 lanes, a
+  // 128-byte line per row), kTallRunGap columns apart within groups of
+  // 4 kTallRunGap columns when n allows; else a quarter of the row apart
+  // when n % 128 == 0; else 128 contiguous columns.  Every form covers each
+  // column once, and a lane keeps its columns in every chunk of the strip.
+  constexpr unsigned SPG = kTallRunGap / 32;   // strips per group
+  int64_t col;
+  if (n % (4u * kTallRunGap) == 0)
+    col = int64_t(it.tj / SPG) * (4 * kTallRunGap) + (ct >> 4) * kTallRunGap +
+          int64_t(it.tj % SPG) * 32 + 2 * (ct & 15);
+  else if (n % 128u == 0)
+    col = int64_t(ct >> 4) * (n / 4) + int64_t(it.tj) * 32 + 2 * (ct & 15);
+  else
+    col = int64_t(it.tj) * kTallCols + 2 * ct;
   const bool act = col < n;
   const unsigned voff = act ? unsigned(col * 4) : 0x80000000u;   // beyond any tile buffer
   const __amdgpu_buffer_rsrc_t rm = tile_rsrc(d.mom + r0 * n, int64_t(rows) * n * 4);

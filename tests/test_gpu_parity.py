@@ -164,7 +164,7 @@ def test_ragged_mixed_set(prec):
     run_direction_parity(RAGGED, 6, ns_precision=prec)
 
 
-TALL = [(1000, 300), (129, 4), (4096, 1024), (520, 516), (32768, 256), (2050, 512)]
+TALL = [(1000, 300), (129, 4), (4096, 1024), (520, 516), (32768, 256), (2050, 512), (2200, 2048)]
 
 
 @pytest.mark.parametrize("single", [1, 0])
@@ -172,10 +172,12 @@ TALL = [(1000, 300), (129, 4), (4096, 1024), (520, 516), (32768, 256), (2050, 51
 def test_tall_rownorm_single_and_two_pass(single, grad_dtype):
     """Long-axis RowNorm of tall matrices in one pass (column statistics
     formed across workgroups) and in two passes, against the oracle: ragged
-    last row chunk (1000, 129, 520, 2050 rows), a part-filled last column
-    strip (300, 516 columns), a 4-column matrix, and the largest strip the
-    single pass takes (32768 rows = 256 chunks).  No workgroup may give up
-    waiting (muon_sync), and the single pass must be the kernel that ran."""
+    last row chunk (1000, 129, 520, 2050, 2200 rows), a part-filled last
+    column strip (300, 516 columns), a 4-column matrix, the largest strip the
+    single pass takes (32768 rows = 128 chunks), and each column layout of a
+    strip (contiguous for n % 128 != 0, runs a quarter row apart for 256, 512
+    and 1024 columns, runs 512 columns apart for 2048).  No workgroup may give
+    up waiting (muon_sync), and the single pass must be the kernel that ran."""
     m = _lib()
     shapes = TALL
     tdt = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
@@ -215,11 +217,12 @@ def test_tall_single_pass_with_two_pass_fallback():
 
 def test_tall_single_pass_repeated_launches():
     """Twenty RowNorm steps in a row on a set of tall matrices (DiT-1.3B
-    qkv, adaLN and fc1 shapes among them): the strip counters return to zero
+    qkv, adaLN and fc1 shapes among them, and 4200 x 4096, whose strips take
+    runs from two 2048-column groups): the strip counters return to zero
     after every launch, so each step matches the two-pass kernels to fp32
     rounding of the column sums, and no wait gives up."""
     m = _lib()
-    shapes = [(6144, 2048), (12288, 2048), (8192, 2048), (1536, 512), (700, 300)]
+    shapes = [(6144, 2048), (12288, 2048), (8192, 2048), (1536, 512), (700, 300), (4200, 4096)]
     out = {}
     for single in (1, 0):
         W = [torch.from_numpy(workloads.host_weight0(3, i, s)).cuda() for i, s in enumerate(shapes)]
