@@ -152,6 +152,14 @@ muon_status muon_state_bytes(const muon_config* cfg, const muon_tensor* params,
 
 /* Build the launch plan, zero all optimizer state and upload the launch
  * tables into the state buffer; waits for hip_stream once before returning.
+ * Source: "Scaling Muon for Diffusion Transformers", English abstract (the
+ * momentum of every 2-D weight is materialised in full, so each matrix gets
+ * an fp32 momentum of its own shape here, zero at init); PaperDaily post,
+ * section "From 1.3B to 15B" (biases and normalisation parameters take
+ * AdamW: kinds[i] = MUON_KIND_ADAMW); section "distributed co-design"
+ * (same-shape matrices are gathered in buckets with a bounded number
+ * materialised at once: here the NS5 problems are grouped into chunks under
+ * ns_workspace_max).
  * params/grads: descriptors of the tensors later steps will pass; their
  *   shapes and dtypes are fixed here, their pointers may change per step.
  *   Matrix params must be F32; grads may be F32 or BF16.
@@ -166,11 +174,21 @@ muon_status muon_init(muon_ctx** out, const muon_config* cfg,
 
 /* Enqueue one optimizer step t >= 0 on the context's stream: updates every
  * param in place and the state in the buffer.  params/grads must match the
- * init-time shapes and dtypes (pointers may differ).  Does not synchronise. */
+ * init-time shapes and dtypes (pointers may differ).  Does not synchronise.
+ * Source: PaperDaily post, section "Periodic Row-wise Muon", blog fig. 3
+ * (M <- beta M + G; t mod K == 0 takes NS5(M), the other steps
+ * gamma * RowNorm_eps(M) of the current momentum; W <- W - lr * U), blog
+ * fig. 4 (RowNorm divides each slice by max(||slice||_2, eps)) and section
+ * "distributed co-design", paper Eq. (8) (tall matrices normalise columns);
+ * "MuonBP: Faster Muon via Block-Periodic Orthogonalization", English
+ * abstract (bp_blocks > 0: per-block NS5 with lr * bp_lr_ratio between full
+ * orthogonalisations). */
 muon_status muon_step(muon_ctx* ctx, const muon_tensor* params,
                       const muon_tensor* grads, int64_t step);
 
-/* A view into the state buffer, for checkpointing and inspection.
+/* A view into the state buffer, for checkpointing and inspection.  Source:
+ * "Scaling Muon for Diffusion Transformers", English abstract (the momentum
+ * is stored explicitly and in full, so it can be read back and restored).
  * which = 0: momentum of a matrix, or AdamW first moment;
  * which = 1: AdamW second moment.  The view is F32, same shape as param i;
  * writing through it (after the stream is idle) restores a checkpoint. */

@@ -265,21 +265,10 @@ def oracle_step(params, grads, state, kinds, t: int, cfg: OracleConfig):
     return new_p, new_s
 
 
-def ns5_flops(m: int, n: int, iters: int = 5) -> float:
-    """Algorithmic flops of one NS5 call on an m x n matrix.
-
-    Per iteration: symmetric Gram r^2 c, symmetric A^2 r^3, product 2 r^2 c,
-    with r = min(m, n), c = max(m, n); the post's review section states the
-    Theta(5 r^2 c) order of this cost.
-    """
-    r, c = min(m, n), max(m, n)
-    return float(iters) * (3.0 * r * r * c + float(r) ** 3)
-
-
 __all__ = [
     "OracleConfig", "BRANCH_ROWNORM", "BRANCH_NS5", "BRANCH_BLOCK_NS5",
     "refresh_indicator", "branch", "momentum_update", "newton_schulz",
     "row_normalize", "column_norms_from_row_shards", "block_newton_schulz",
-    "direction", "muon_matrix_step", "adamw_step", "oracle_step", "ns5_flops",
+    "direction", "muon_matrix_step", "adamw_step", "oracle_step",
 ]
 

@@ -308,22 +308,113 @@ def test_adamw_constant_gradient_is_signed_step():
         np.testing.assert_allclose(p, -cfg.adam_lr * (t + 1) * np.sign(g), rtol=1e-12)
 
 
+# ------------------------------------------------------------------ whole parameter list
+def test_oracle_step_on_a_mixed_list():
+    """oracle_step over a list that mixes a wide and a tall Muon matrix with
+    two AdamW vectors, for two K-cycles.  Each entry is checked against a
+    route that does not go through the oracle: the matrices against the
+    discounted gradient sum put through the SVD closed form (refresh steps)
+    or divided by its long-axis slice norms (RowNorm steps), the vectors
+    against torch.optim.AdamW; the returned state keeps the per-entry kind
+    (momentum array, or the AdamW (m, v) pair in that order)."""
+    rng = _rng(19)
+    cfg = oracle.OracleConfig(adam_lr=2e-3, adam_wd=0.01)
+    shapes = [(9, 21), None, (30, 8), None]
+    kinds = ["matrix", "adamw", "matrix", "adamw"]
+    sizes = {1: 13, 3: 40}
+    params = [rng.standard_normal(s) * 0.02 if k == "matrix" else rng.standard_normal(sizes[i])
+              for i, (s, k) in enumerate(zip(shapes, kinds))]
+    state = [np.zeros(s) if k == "matrix" else (np.zeros(sizes[i]), np.zeros(sizes[i]))
+             for i, (s, k) in enumerate(zip(shapes, kinds))]
+    torch_p = {i: torch.tensor(params[i], dtype=torch.float64, requires_grad=True) for i in sizes}
+    opts = {i: torch.optim.AdamW([torch_p[i]], lr=cfg.adam_lr, betas=(cfg.adam_b1, cfg.adam_b2),
+                                 eps=cfg.adam_eps, weight_decay=cfg.adam_wd) for i in sizes}
+    W0 = [p.copy() for p in params]
+    gsum = {0: [], 2: []}
+    for t in range(2 * cfg.K):
+        grads = [rng.standard_normal(s) if k == "matrix" else rng.standard_normal(sizes[i])
+                 for i, (s, k) in enumerate(zip(shapes, kinds))]
+        before = [np.copy(p) for p in params]
+        params, state = oracle.oracle_step(params, grads, state, kinds, t, cfg)
+        for i in sizes:
+            torch_p[i].grad = torch.tensor(grads[i], dtype=torch.float64)
+            opts[i].step()
+            np.testing.assert_allclose(params[i], torch_p[i].detach().numpy(), rtol=1e-13, atol=1e-15)
+            # (m, v) in that order: discounted sums of the gradients and of their squares
+            gsum.setdefault(i, []).append(grads[i])
+            m_ref = sum((1 - cfg.adam_b1) * cfg.adam_b1 ** (t - s) * g for s, g in enumerate(gsum[i]))
+            v_ref = sum((1 - cfg.adam_b2) * cfg.adam_b2 ** (t - s) * g * g
+                        for s, g in enumerate(gsum[i]))
+            np.testing.assert_allclose(state[i][0], m_ref, rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(state[i][1], v_ref, rtol=1e-12, atol=1e-15)
+        for i in (0, 2):
+            gsum[i].append(grads[i])
+            Mref = sum(0.95 ** (t - s) * g for s, g in enumerate(gsum[i]))
+            np.testing.assert_allclose(state[i], Mref, rtol=1e-12, atol=1e-14)
+            U = (before[i] - params[i]) / cfg.lr
+            if t % cfg.K == 0:
+                np.testing.assert_allclose(U, ns_via_svd(Mref), atol=1e-12)
+            else:
+                axis = 0 if shapes[i][0] > shapes[i][1] else 1
+                norms = np.linalg.norm(Mref, axis=axis, keepdims=True)
+                np.testing.assert_allclose(U, cfg.gamma * Mref / norms, rtol=1e-12, atol=1e-15)
+    for i in (0, 2):
+        assert not np.allclose(params[i], W0[i])
+    # the inputs are not modified
+    p_in = [np.ones((3, 5)), np.ones(4)]
+    s_in = [np.zeros((3, 5)), (np.zeros(4), np.zeros(4))]
+    oracle.oracle_step(p_in, [np.ones((3, 5)), np.ones(4)], s_in, ["matrix", "adamw"], 1, cfg)
+    assert np.all(p_in[0] == 1) and np.all(s_in[0] == 0) and np.all(s_in[1][0] == 0)
+
+
 # ------------------------------------------------------------------ planted mistakes
 def test_pins_catch_planted_mistakes():
-    """Mistakes planted in copies of the oracle's arithmetic are caught."""
-    M = _rng(18).standard_normal((12, 30))
-    ref = ns_via_svd(M)
+    """Mistakes planted in copies of the oracle's arithmetic are caught by
+    the pins above: the NS5 variants by the SVD closed form, the RowNorm
+    variants by the pages' sqrt(r) Frobenius norm, the long-axis unit norms
+    and the Eq. (8) column statistics."""
+    rng = _rng(18)
+    M = rng.standard_normal((12, 30))
+    S = rng.standard_normal((16, 16))          # square: transposed operands type-check
 
-    def ns_variant(M, swap=False, iters=5, sign=1.0, normalise=True):
+    def ns_variant(M, swap=False, iters=5, sign=1.0, normalise=True, right=False, gram_t=False):
         X = M / (np.linalg.norm(M) + 1e-7) if normalise else M
         for _ in range(iters):
-            A = X @ X.T
+            A = X.T @ X if gram_t else X @ X.T
             B = (C5 * A + B5 * (A @ A)) if swap else (B5 * A + sign * C5 * (A @ A))
-            X = A5 * X + B @ X
+            X = A5 * X + (X @ B if right else B @ X)
         return X
 
-    assert np.allclose(ns_variant(M), ref, atol=1e-12)
-    for kw in (dict(swap=True), dict(iters=4), dict(sign=-1.0), dict(normalise=False)):
+    for inp in (M, S):
+        assert np.allclose(ns_variant(inp), ns_via_svd(inp), atol=1e-12)
+    for inp, kw in [(M, dict(swap=True)), (M, dict(iters=4)), (M, dict(sign=-1.0)),
+                    (M, dict(normalise=False)), (S, dict(right=True)), (S, dict(gram_t=True))]:
         with np.errstate(all="ignore"):
-            bad = ns_variant(M, **kw)
-        assert not np.allclose(bad, ref, atol=1e-3)
+            bad = ns_variant(inp, **kw)
+        assert not np.allclose(bad, ns_via_svd(inp), atol=1e-3), kw
+
+    # RowNorm of a tall matrix along the wrong (stored-row) axis, without the
+    # eps floor's max, or with the norm squared
+    T = rng.standard_normal((40, 9))
+    r = min(T.shape)
+
+    def rn_variant(X, axis=0, floor=True, power=0.5):
+        s = np.sum(X * X, axis=axis, keepdims=True) ** power
+        return X / (np.maximum(s, 1e-8) if floor else s)
+
+    def pins_hold(R, X):
+        unit = np.allclose(np.linalg.norm(R, axis=0), 1.0, atol=1e-12)
+        frob = abs(np.linalg.norm(R) - np.sqrt(r)) < 1e-12
+        nu = oracle.column_norms_from_row_shards(X, [np.arange(0, 17), np.arange(17, 40)])
+        eq8 = np.allclose(R, X / nu, rtol=1e-12)
+        return unit and frob and eq8
+
+    assert pins_hold(rn_variant(T), T) and pins_hold(oracle.row_normalize(T), T)
+    for kw in (dict(axis=1), dict(power=1.0)):
+        assert not pins_hold(rn_variant(T, **kw), T), kw
+    Z = T.copy()
+    Z[:, 4] = 0.0
+    with np.errstate(all="ignore"):
+        no_floor = rn_variant(Z, floor=False)
+    assert not np.all(np.isfinite(no_floor))          # the zero-slice pin fails
+    assert not np.any(oracle.row_normalize(Z)[:, 4])
