@@ -72,17 +72,22 @@ def cnt_per(name: str, cfg) -> int:
     return cfg.ns_iters - 1 if name == "ns_product" else cfg.ns_iters
 
 
-def source_digest() -> str:
-    """sha256 over the device code (csrc/*.hip and the header they share),
-    so that counter figures taken on other kernels are not reported.  Host
-    code (the launch planner) is left out: the counters follow the kernels."""
+KERNEL_SOURCES = {"ns_": "kernels_ns5.hip", "rownorm_": "kernels_rownorm.hip",
+                  "adamw": "kernels_misc.hip"}
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 over the device source of `kernel` (the .hip file that holds it
+    and the header of structures it shares with the planner), so that counter
+    figures taken on other code are not reported.  Host code (the launch
+    planner) is left out: the counters follow the kernels."""
     import hashlib
     d = os.path.join(HERE, "matrix_aware_optimizer_periodic_amd", "csrc")
+    src = next(f for p, f in KERNEL_SOURCES.items() if kernel.startswith(p))
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in (src, "muon_internal.h"):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()
 
 
@@ -98,7 +103,7 @@ def measured_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != source_digest():
+    if kv.get("source_sha256") != source_digest(kernel):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -127,8 +132,17 @@ def rownorm_class_bytes(shapes, gbytes, single_pass=True):
             "rownorm_tall": tall}
 
 
-def cpu_baseline(wl, cfg_over, sample_blocks=1):
-    """The fp64 oracle as it stands, one K-cycle on a sample of blocks."""
+def cpu_baseline(wl, cfg_over, flop_budget=1.2e13):
+    """The fp64 oracle as it stands, timed on one K-cycle of a sample of the
+    set, then scaled to the whole set per branch.
+
+    The sample is the first block's matrices, taken in the order proj, qkv,
+    fc1, fc2, adaLN while their NS5 flops stay within ``flop_budget`` (on
+    DiT-15B: proj and qkv, one wide and one tall matrix; on DiT-1.3B the
+    whole block; a single-matrix set as it is).  Refresh steps (and MuonBP
+    block steps) are scaled by algorithmic NS5 flops, RowNorm steps by
+    elements, and the cycle average is paper Eq. (9)'s:
+    K / (t_refresh + (K - 1) t_other)."""
     import oracle
     blas = "unknown"
     try:
@@ -148,38 +162,71 @@ def cpu_baseline(wl, cfg_over, sample_blocks=1):
     except OSError:
         pass
     ocfg = oracle.OracleConfig(**cfg_over)
-    sample_blocks = min(sample_blocks, wl.blocks or 1)
-    per_block = len(workloads.dit_block_shapes(wl.d)) if wl.d else len(wl.shapes)
-    shapes = [(m, n) for _, m, n in wl.shapes[:per_block * sample_blocks]]
+    all_shapes = [(m, n) for _, m, n in wl.shapes]
+    if wl.d:
+        block = [(lab, m, n) for lab, m, n in wl.shapes[:len(workloads.dit_block_shapes(wl.d))]]
+        order = {"proj": 0, "qkv": 1, "fc1": 2, "fc2": 3, "adaln": 4}
+        block.sort(key=lambda x: order.get(x[0].split(".")[-1], 9))
+        idx, shapes, f = [], [], 0.0
+        for k, (lab, m, n) in enumerate(block):
+            fk = sum(ns5_class_flops([(m, n)], ocfg.ns_iters).values())
+            if shapes and f + fk > flop_budget:
+                break
+            idx.append(k)
+            shapes.append((m, n))
+            f += fk
+        labels = [block[k][0].split(".")[-1] for k in idx]
+    else:
+        shapes, labels = list(all_shapes), [lab for lab, _, _ in wl.shapes]
     W = [workloads.host_weight0(0, i, s).astype(np.float64) for i, s in enumerate(shapes)]
     M = [np.zeros(s) for s in shapes]
     G = [workloads.host_grad(0, 0, i, s, wl.grad_std, wl.grad_dtype) for i, s in enumerate(shapes)]
     K = ocfg.K if ocfg.bp_blocks == 0 else ocfg.bp_period
 
-    def cycles():
-        """Whole K-cycles (at least one, more while under a second) -> s/cycle."""
-        n, t0 = 0, time.perf_counter()
-        while n == 0 or time.perf_counter() - t0 < 1.0:
-            for t in range(K):
-                for i in range(len(shapes)):
-                    W[i], M[i], _ = oracle.muon_matrix_step(W[i], M[i], G[i], t, ocfg)
-            n += 1
-        return (time.perf_counter() - t0) / n, n
+    def one_step(t):
+        t0 = time.perf_counter()
+        for i in range(len(shapes)):
+            W[i], M[i], _ = oracle.muon_matrix_step(W[i], M[i], G[i], t, ocfg)
+        return time.perf_counter() - t0
 
-    dt, ncyc = cycles()
-    scale = (wl.blocks / sample_blocks) if wl.blocks else 1.0
-    steps_per_s = K / (dt * scale)
-    out = {"value": steps_per_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+    # one K-cycle (repeated while under a second, for the single small matrix)
+    per_branch, t, t_start = {}, 0, time.perf_counter()
+    while t < K or time.perf_counter() - t_start < 1.0:
+        per_branch.setdefault(oracle.branch(t, ocfg), []).append(one_step(t))
+        t += 1
+    sample_seconds = time.perf_counter() - t_start
+
+    def ns_flops(shp):
+        return sum(ns5_class_flops(shp, ocfg.ns_iters).values())
+
+    def blocks_of(shp):
+        return [(m, n // ocfg.bp_blocks) for m, n in shp for _ in range(ocfg.bp_blocks)]
+
+    scale = {oracle.BRANCH_NS5: ns_flops(all_shapes) / ns_flops(shapes),
+             oracle.BRANCH_ROWNORM: sum(m * n for m, n in all_shapes) / sum(m * n for m, n in shapes)}
+    if ocfg.bp_blocks:
+        scale[oracle.BRANCH_BLOCK_NS5] = ns_flops(blocks_of(all_shapes)) / ns_flops(blocks_of(shapes))
+    t_branch = {b: float(np.mean(v)) * scale[b] for b, v in per_branch.items()}
+    other = oracle.BRANCH_BLOCK_NS5 if ocfg.bp_blocks else oracle.BRANCH_ROWNORM
+    cycle_s = t_branch[oracle.BRANCH_NS5] + (K - 1) * t_branch.get(other, 0.0)
+    names = {0: "rownorm", 1: "ns5", 2: "block_ns5"}
+    exact = all(abs(v - 1.0) < 1e-12 for v in scale.values())
+    out = {"value": K / cycle_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
            "cpu": cpu_model, "blas": blas, "numpy": np.__version__,
-           "sample": f"{len(shapes)} matrices ({sample_blocks} of {wl.blocks or 1} blocks), "
-                     f"{K}-step cycle x{ncyc}, {dt:.3g} s per cycle, scaled x{scale:g} to the whole set",
-           "sample_seconds": dt * ncyc}
+           "sample": (f"{len(shapes)} of {len(all_shapes)} matrices ({', '.join(labels)} of one "
+                      f"block), {t} steps (t=0..{t - 1}); per-step times "
+                      + ("of the whole set" if exact else
+                         "extrapolated to the whole set by NS5 flops (refresh steps) and "
+                         "elements (RowNorm steps)")
+                      + f"; Eq. (9) cycle average over K={K}"),
+           "branch_s": {names[b]: v for b, v in t_branch.items()},
+           "sample_seconds": sample_seconds}
     if not wl.blocks:
         # the single-matrix set is small enough to time on one core as well
         try:
             from threadpoolctl import threadpool_limits
             with threadpool_limits(limits=1):
-                dt1, _ = cycles()
+                dt1 = sum(one_step(k) for k in range(K))
             out["value_1core"] = K / dt1
         except Exception:
             pass
@@ -201,18 +248,21 @@ def copy_calibration(nbytes: int, reps: int) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=12)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dit-1.3b", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", default="dit-15b", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--ns-precision", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--K", type=int, default=None, help="refresh period (default 3)")
     ap.add_argument("--no-adamw", action="store_true", help="leave out the bias vectors")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=2)
+    ap.add_argument("--cpu-flop-budget", type=float, default=1.2e13,
+                    help="NS5 flops of the oracle's sample of matrices")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--ws-gib", type=float, default=None, help="NS5 workspace cap (GiB)")
     ap.add_argument("--tall-two-pass", action="store_true",
                     help="tall RowNorm in two passes instead of one")
+    ap.add_argument("--print-digest", default="", metavar="KERNEL",
+                    help="only print the device-source digest that keys KERNEL's counters")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter scaling)")
     args = ap.parse_args()
@@ -228,6 +278,9 @@ def main() -> int:
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
+        return 0
+    if args.print_digest:
+        print(source_digest(args.print_digest))
         return 0
 
     wl = workloads.WORKLOADS[args.workload]
@@ -387,9 +440,21 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         ocfg = {k: v for k, v in over.items() if k in ("K", "bp_blocks", "bp_period", "bp_lr_ratio")}
-        cpu = cpu_baseline(wl, ocfg, args.cpu_sample_blocks)
+        cpu = cpu_baseline(wl, ocfg, args.cpu_flop_budget)
 
-    value = args.steps / (total_ms * 1e-3)
+    # Paper Eq. (9): one refresh and K - 1 other steps per cycle, from the
+    # mean time of each branch over the timed steps, so that a timed window
+    # that does not start or end on a cycle boundary still gives the cycle
+    # average.  Without every branch in the window: the plain mean.
+    other = mm.MUON_BRANCH_BLOCK_NS5 if cfg.bp_blocks else mm.MUON_BRANCH_ROWNORM
+    if K == 1 and "ns5" in branch_ms:
+        cycle_ms, value_kind = branch_ms["ns5"], "every step refreshes (K = 1)"
+    elif "ns5" in branch_ms and names[other] in branch_ms:
+        cycle_ms = (branch_ms["ns5"] + (K - 1) * branch_ms[names[other]]) / K
+        value_kind = f"Eq. (9) cycle average: (t_ns5 + {K - 1} t_{names[other]}) / {K}"
+    else:
+        cycle_ms, value_kind = total_ms / args.steps, "mean over the timed steps (not a whole cycle)"
+    value = 1e3 / cycle_ms
     out = {
         "metric": METRIC,
         "value": value,
@@ -397,7 +462,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": total_ms / args.steps,
+        "ms_per_step": cycle_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -416,6 +481,8 @@ def main() -> int:
             "bp_blocks": cfg.bp_blocks, "adamw_tensors": n_bias, "adamw_elements": bias_elems,
             "ns_workspace_max": int(cfg.ns_workspace_max), "state_bytes": sess.state_bytes,
         },
+        "value_kind": value_kind,
+        "timed_total_ms": total_ms,
         "branch_ms": branch_ms,
         "ns5": ns5,
         "block_ns5": block_ns5,
