@@ -200,15 +200,27 @@ muon_status muon_state(const muon_ctx* ctx, int32_t i, int32_t which,
  * refreshes; MuonBP abstract for the block variant). */
 int32_t muon_branch(const muon_config* cfg, int64_t step);
 
-/* Wait for the context's stream, then report what the device recorded.
- * MUON_E_HIP: the wait failed (a kernel fault or an earlier HIP error).
- * MUON_E_STATE: in some step since muon_init, a workgroup of the
- *   single-pass tall RowNorm kernel stopped waiting for its column strip
- *   after its poll limit (possible only when other work holds most of the
- *   device's compute units, so that a strip's workgroups cannot all be
- *   resident); the weights of that step are wrong.  The library never
- *   waits on the host otherwise; call this where a check is wanted. */
+/* Wait for the context's stream.  MUON_E_HIP if the wait failed (a kernel
+ * fault or an earlier HIP error).  The library never waits on the host
+ * otherwise; call this where a check is wanted. */
 muon_status muon_sync(muon_ctx* ctx);
+
+/* The single-pass tall RowNorm forms each column strip's norms across
+ * workgroups (the post's section "distributed co-design", paper Eq. (8):
+ * column sums of squares over row shards, added up).  A workgroup waits for
+ * its strip's sum; after `polls` polls (default 262144, about half a
+ * second) it stops waiting, leaves its tile of W alone and lists it, and a
+ * repair launch that muon_step enqueues right after writes the listed tiles
+ * with the same arithmetic, bit for bit.  A wait can only reach the limit
+ * when other work holds most of the device's compute units.  polls = 0
+ * makes every wait give up at once (for testing the repair path).  Host
+ * only; applies to steps enqueued after the call. */
+muon_status muon_tall_poll_limit(muon_ctx* ctx, uint32_t polls);
+
+/* Waits for the context's stream, then writes to *count how many waits of
+ * the single-pass tall RowNorm have given up (and been repaired) since
+ * muon_init.  MUON_E_HIP if the wait or the read failed. */
+muon_status muon_tall_giveups(muon_ctx* ctx, uint64_t* count);
 
 /* Release host-side plan memory.  Does not touch the state buffer or the
  * stream; the caller must not free the state buffer while the stream still
@@ -237,7 +249,8 @@ typedef enum muon_kernel_class {
   MUON_K_ADAMW = 9,          /* AdamW on the non-matrix tensors              */
   MUON_K_ROWNORM_COEF = 10,  /* RowNorm step, tall: column coefficients      */
   MUON_K_ROWNORM_TALL = 11,  /* RowNorm step, tall, single pass              */
-  MUON_K_COUNT = 12
+  MUON_K_ROWNORM_REPAIR = 12,/* RowNorm step, tall: tiles whose wait gave up */
+  MUON_K_COUNT = 13
 } muon_kernel_class;
 
 /* While enabled (enable != 0), muon_step records a HIP event before and

@@ -13,8 +13,9 @@ from .binding import (  # noqa: F401
     EXPORTED, KERNEL_CLASSES, MUON_BF16, MUON_BRANCH_BLOCK_NS5, MUON_BRANCH_NS5, MUON_BRANCH_ROWNORM, MUON_F32,
     MUON_KIND_ADAMW, MUON_KIND_MATRIX, MUON_NS_BF16, MUON_NS_F32, MuonConfig, MuonError,
     MuonTensor, lib, muon_branch, muon_config_default, muon_free, muon_init, muon_last_error,
-    muon_state, muon_state_bytes, muon_status_str, muon_step, muon_sync, muon_timing_enable,
-    muon_timing_read, tensor_desc)
+    muon_state, muon_state_bytes, muon_status_str, muon_step, muon_sync,
+    muon_tall_giveups,
+    muon_tall_poll_limit, muon_timing_enable, muon_timing_read, tensor_desc)
 
 
 class MuonSession:
@@ -62,8 +63,12 @@ class MuonSession:
         return t.view(v.rows, v.cols) if self.params[i].dim() == 2 else t.view(self.params[i].shape)
 
     def sync(self) -> None:
-        """Wait for the stream; raises if the device recorded a failed wait."""
+        """Wait for the stream; raises if a kernel failed."""
         muon_sync(self.ctx)
+
+    def tall_giveups(self) -> int:
+        """Waits of the single-pass tall RowNorm that gave up (and were repaired)."""
+        return muon_tall_giveups(self.ctx)
 
     def branch(self, t: int) -> int:
         return muon_branch(self.cfg, t)

@@ -23,12 +23,13 @@ MUON_NS_BF16, MUON_NS_F32 = 0, 1
 
 EXPORTED = ("muon_config_default", "muon_state_bytes", "muon_init", "muon_step", "muon_state",
             "muon_branch", "muon_free", "muon_status_str", "muon_last_error",
-            "muon_timing_enable", "muon_timing_read", "muon_sync")
+            "muon_timing_enable", "muon_timing_read", "muon_sync", "muon_tall_poll_limit",
+            "muon_tall_giveups")
 
 # muon_kernel_class, in enum order
 KERNEL_CLASSES = ("rownorm_rows", "rownorm_cols1", "rownorm_cols2", "ns_prep", "ns_scale",
                   "ns_gram", "ns_poly", "ns_product", "ns_product_last", "adamw", "rownorm_coef",
-                  "rownorm_tall")
+                  "rownorm_tall", "rownorm_repair")
 
 
 class MuonTensor(ctypes.Structure):
@@ -120,6 +121,10 @@ def lib() -> ctypes.CDLL:
         L.muon_timing_read.restype = ctypes.c_int
         L.muon_sync.argtypes = [ctypes.c_void_p]
         L.muon_sync.restype = ctypes.c_int
+        L.muon_tall_poll_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
+        L.muon_tall_poll_limit.restype = ctypes.c_int
+        L.muon_tall_giveups.argtypes = [ctypes.c_void_p, P(ctypes.c_uint64)]
+        L.muon_tall_giveups.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -223,5 +228,15 @@ def muon_timing_read(ctx) -> dict:
 
 
 def muon_sync(ctx) -> None:
-    """Wait for the context's stream; raises MuonError on what the device recorded."""
+    """Wait for the context's stream; raises MuonError if the wait failed."""
     _check(lib().muon_sync(ctx), ctx)
+
+
+def muon_tall_poll_limit(ctx, polls: int) -> None:
+    _check(lib().muon_tall_poll_limit(ctx, int(polls)), ctx)
+
+
+def muon_tall_giveups(ctx) -> int:
+    out = ctypes.c_uint64(0)
+    _check(lib().muon_tall_giveups(ctx, ctypes.byref(out)), ctx)
+    return out.value

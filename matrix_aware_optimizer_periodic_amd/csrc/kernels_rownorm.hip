@@ -426,8 +426,11 @@ __global__ __launch_bounds__(kThreads) void rownorm_coef_kernel(
 // the strip's workgroups all start and arrive, and by induction every strip
 // does.  (Ids claimed at run time from a counter would not do: near the end
 // of a launch the XCD with workgroups left would have to hold whole strips.)
-// A wait still gives up after kTallSpinMax polls and counts that in
-// *giveups, which the host reports.
+// A wait still gives up after a poll limit (kTallPollLimit by default): the
+// workgroup then leaves W alone and lists its tile, and a repair launch on
+// the same stream writes the listed tiles once every strip's coefficients
+// are published (they always are by the end of the launch, since arrivals
+// never wait).  The result is the same either way, bit for bit.
 //
 // Partials and coefficients cross workgroups, and with them the XCDs'
 // separate L2 caches, within the launch.  Each strip owns padded rows of its
@@ -445,7 +448,6 @@ __global__ __launch_bounds__(kThreads) void rownorm_coef_kernel(
 constexpr int kTallThreads = 512;
 constexpr int kTallRowsPerThread = kTallRows / (kTallThreads / 64);   // 32
 constexpr int kTallBatch = 8;                                         // rows per load batch
-constexpr uint32_t kTallSpinMax = 1u << 18;   // about 0.5 s of polling
 static_assert(kTallCols == 2 * 64, "two columns per lane");
 constexpr unsigned kTallRunGap = 512;   // columns between a strip's runs
 static_assert(kTallRunGap % 32 == 0, "whole runs");
@@ -558,15 +560,31 @@ __device__ __forceinline__ void tall_momentum(const void* g, __amdgpu_buffer_rsr
   }
 }
 
+// Column of lane ct (0..63, two columns col and col + 1) in column strip tj
+// of an n-column matrix: four runs of 32 (one per group of 16 lanes, a
+// 128-byte line per row), kTallRunGap columns apart within groups of
+// 4 kTallRunGap columns when n allows; else a quarter of the row apart when
+// n % 128 == 0; else 128 contiguous columns.  Every form covers each column
+// once, and a lane keeps its columns in every chunk of the strip.
+__device__ __forceinline__ int64_t tall_col(unsigned tj, int ct, unsigned n) {
+  constexpr unsigned SPG = kTallRunGap / 32;   // strips per group
+  if (n % (4u * kTallRunGap) == 0)
+    return int64_t(tj / SPG) * (4 * kTallRunGap) + (ct >> 4) * kTallRunGap +
+           int64_t(tj % SPG) * 32 + 2 * (ct & 15);
+  if (n % 128u == 0) return int64_t(ct >> 4) * (n / 4) + int64_t(tj) * 32 + 2 * (ct & 15);
+  return int64_t(tj) * kTallCols + 2 * ct;
+}
+
 __global__ __launch_bounds__(kTallThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __restrict__ tiles,
-                         TallSync* __restrict__ sync, uint32_t* __restrict__ giveups,
+                         TallSync* __restrict__ sync, TallCtl* __restrict__ ctl,
+                         uint32_t* __restrict__ repair, uint32_t ntiles, uint32_t poll_limit,
                          StepScalars sc) {
   constexpr int RPT = kTallRowsPerThread;
   constexpr int B = kTallBatch;
   __shared__ float2 red[kTallThreads / 64][64];
   __shared__ float2 cf[64];
-  __shared__ uint32_t s_reducer;
+  __shared__ uint32_t s_reducer, s_gaveup;
   const int tid = threadIdx.x;
   const TileItem it = tiles[blockIdx.x];
   const MatDev d = mats[it.id];
@@ -577,20 +595,7 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
   const int64_t r0 = int64_t(it.ti) * kTallRows;
   const int rows = int(min(m, r0 + kTallRows) - r0);
   const int rg = __builtin_amdgcn_readfirstlane(tid >> 6), ct = tid & 63;
-  // Columns of strip tj: four runs of 32 (one per group of 16 lanes, a
-  // 128-byte line per row), kTallRunGap columns apart within groups of
-  // 4 kTallRunGap columns when n allows; else a quarter of the row apart
-  // when n % 128 == 0; else 128 contiguous columns.  Every form covers each
-  // column once, and a lane keeps its columns in every chunk of the strip.
-  constexpr unsigned SPG = kTallRunGap / 32;   // strips per group
-  int64_t col;
-  if (n % (4u * kTallRunGap) == 0)
-    col = int64_t(it.tj / SPG) * (4 * kTallRunGap) + (ct >> 4) * kTallRunGap +
-          int64_t(it.tj % SPG) * 32 + 2 * (ct & 15);
-  else if (n % 128u == 0)
-    col = int64_t(ct >> 4) * (n / 4) + int64_t(it.tj) * 32 + 2 * (ct & 15);
-  else
-    col = int64_t(it.tj) * kTallCols + 2 * ct;
+  const int64_t col = tall_col(unsigned(it.tj), ct, n);
   const bool act = col < n;
   const unsigned voff = act ? unsigned(col * 4) : 0x80000000u;   // beyond any tile buffer
   const __amdgpu_buffer_rsrc_t rm = tile_rsrc(d.mom + r0 * n, int64_t(rows) * n * 4);
@@ -634,6 +639,7 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
     if (rg + 8 * u < rows) bst2_guarded(rm, voff, tall_row(rg, u, rows, n, 4), mv[u]);
   __syncthreads();
   float2 coef;
+  bool skip_w = false;
   if (__builtin_amdgcn_readfirstlane(s_reducer)) {
     // 3a. last arrival: every partial of the strip is published.
     __syncthreads();
@@ -667,19 +673,29 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
     __syncthreads();
     coef = cf[ct];
   } else {
-    // 3b. wait for the strip's coefficients.
+    // 3b. wait for the strip's coefficients; a wait that gives up lists the
+    //     tile for the repair launch instead of writing W.
     if (tid == 0) {
-      uint32_t spins = 0;
+      uint32_t spins = 0, gave_up = 0;
       while (rd_counter(&sy->ready) == 0u) {
-        if (++spins > kTallSpinMax) { atomicAdd(giveups, 1u); break; }
+        if (++spins > poll_limit) { gave_up = 1; break; }
         __builtin_amdgcn_s_sleep(10);   // about 640 clocks between polls
       }
+      if (gave_up) {
+        atomicAdd(&ctl->giveups, 1u);
+        const uint32_t slot = atomicAdd(&ctl->repair_count, 1u);
+        if (slot < ntiles) repair[slot] = blockIdx.x;
+      }
+      s_gaveup = gave_up;
     }
     __syncthreads();
-    coef = ld2_agent(sp + int64_t(nchunk) * kTallCols);
+    skip_w = __builtin_amdgcn_readfirstlane(s_gaveup) != 0;
+    coef = skip_w ? make_float2(0.f, 0.f) : ld2_agent(sp + int64_t(nchunk) * kTallCols);
   }
-  // 4. W <- W (1 - lr wd) - coef M, loads of 8 rows ahead of their stores.
+  // 4. W <- W (1 - lr wd) - coef M, loads of 8 rows ahead of their stores
+  //    (skipped by a workgroup whose wait gave up: the repair launch does it).
   const float wkeep = 1.0f - sc.lr * sc.wd;
+  if (!skip_w) {
 #pragma unroll
   for (int b = 0; b < RPT; b += B) {
     if (b > 0) {
@@ -695,6 +711,7 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
                                  fmaf(-coef.y, mm.y, ww.y * wkeep)));
     }
   }
+  }
   // 5. leave the strip; the last one out clears it for the next launch.
   __syncthreads();   // every thread holds its coefficients
   if (tid == 0) {
@@ -702,6 +719,52 @@ void rownorm_tall_kernel(const MatDev* __restrict__ mats, const TileItem* __rest
       set_counter(&sy->depart, 0u);
       set_counter(&sy->ready, 0u);
     }
+  }
+}
+
+// Repair launch of the single-pass tall RowNorm, enqueued right after it:
+// the tiles whose workgroup gave up waiting get W <- W (1 - lr wd) - coef M
+// from the strip's published coefficients and the momentum that workgroup
+// stored, with the arithmetic of the normal path, so the result is the
+// same bit for bit.  Every workgroup reads the list length first; the last
+// one to finish resets it (and its own counter) for the next launch, so no
+// launch needs clearing.  With nothing listed each workgroup exits after a
+// load and an atomic.
+__global__ __launch_bounds__(kTallThreads) void rownorm_tall_repair_kernel(
+    const MatDev* __restrict__ mats, const TileItem* __restrict__ tiles,
+    TallCtl* __restrict__ ctl, const uint32_t* __restrict__ repair, uint32_t ntiles,
+    StepScalars sc) {
+  __shared__ uint32_t s_count;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_count = min(rd_counter(&ctl->repair_count), ntiles);
+  __syncthreads();
+  const uint32_t count = s_count;
+  const int rg = tid >> 6, ct = tid & 63;
+  const float wkeep = 1.0f - sc.lr * sc.wd;
+  for (uint32_t k = blockIdx.x; k < count; k += gridDim.x) {
+    const TileItem it = tiles[repair[k]];
+    const MatDev d = mats[it.id];
+    const int64_t m = d.rows;
+    const unsigned n = unsigned(d.cols);
+    const uint32_t nchunk = static_cast<uint32_t>((m + kTallRows - 1) / kTallRows);
+    const int64_t r0 = int64_t(it.ti) * kTallRows;
+    const int rows = int(min(m, r0 + kTallRows) - r0);
+    const int64_t col = tall_col(unsigned(it.tj), ct, n);
+    if (col >= n) continue;
+    const float2 coef = ld2_agent(d.part + int64_t(it.tj) * (nchunk + 1) * kTallCols + 2 * ct +
+                                  int64_t(nchunk) * kTallCols);
+    for (int r = rg; r < rows; r += kTallThreads / 64) {
+      const int64_t e = (r0 + r) * n + col;
+      const float2 mm = make_float2(d.mom[e], d.mom[e + 1]);
+      const float2 ww = make_float2(d.w[e], d.w[e + 1]);
+      d.w[e] = fmaf(-coef.x, mm.x, ww.x * wkeep);
+      d.w[e + 1] = fmaf(-coef.y, mm.y, ww.y * wkeep);
+    }
+  }
+  __syncthreads();   // every thread is done with the list
+  if (tid == 0 && atomicAdd(&ctl->repair_done, 1u) == gridDim.x - 1) {
+    set_counter(&ctl->repair_count, 0u);
+    set_counter(&ctl->repair_done, 0u);
   }
 }
 
@@ -745,11 +808,21 @@ hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem
 }
 
 hipError_t launch_rownorm_tall(hipStream_t s, const MatDev* mats, const TileItem* tiles,
-                               int64_t ntiles, TallSync* sync, uint32_t* giveups,
-                               StepScalars sc) {
+                               int64_t ntiles, TallSync* sync, TallCtl* ctl, uint32_t* repair,
+                               uint32_t poll_limit, StepScalars sc) {
   if (ntiles <= 0) return hipSuccess;
   rownorm_tall_kernel<<<dim3(static_cast<unsigned>(ntiles)), dim3(kTallThreads), 0, s>>>(
-      mats, tiles, sync, giveups, sc);
+      mats, tiles, sync, ctl, repair, static_cast<uint32_t>(ntiles), poll_limit, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_rownorm_repair(hipStream_t s, const MatDev* mats, const TileItem* tiles,
+                                 int64_t ntiles, TallCtl* ctl, const uint32_t* repair,
+                                 StepScalars sc) {
+  if (ntiles <= 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>(ntiles < 256 ? ntiles : 256);
+  rownorm_tall_repair_kernel<<<dim3(grid), dim3(kTallThreads), 0, s>>>(
+      mats, tiles, ctl, repair, static_cast<uint32_t>(ntiles), sc);
   return hipGetLastError();
 }
 

@@ -34,6 +34,19 @@ struct TallSync {
   uint32_t pad[29];
 };
 
+// Control line of the single-pass tall RowNorm, followed in the state
+// buffer by its repair list (one uint32 per tile).  A workgroup whose wait
+// for its strip gives up does not write W: it appends its tile index to the
+// list, and the repair launch that follows on the same stream applies the
+// W update of the listed tiles (the strip's coefficients are published by
+// then).  repair_count and repair_done are zero between launch pairs.
+struct TallCtl {
+  uint32_t repair_count;   // tiles listed in this launch
+  uint32_t giveups;        // waits that gave up since init (never reset)
+  uint32_t repair_done;    // repair workgroups finished
+  uint32_t pad[29];
+};
+
 // One AdamW tensor (flattened).
 struct AdamDev {
   float* p;
@@ -120,11 +133,16 @@ hipError_t launch_rownorm_cols(hipStream_t s, const MatDev* mats, const TileItem
                                int64_t ntiles, int phase, StepScalars sc);
 // Column-normalised (tall) matrices in one pass: tiles kTallRows x
 // kTallCols listed strip by strip (row chunks of a strip consecutive),
-// one workgroup per tile.  *giveups counts waits that gave up (zero unless
-// the residency bound is broken).
+// one workgroup per tile.  A wait gives up after poll_limit polls (that
+// happens only when the residency bound is broken, or in tests that set a
+// small limit) and lists its tile in `repair` instead of writing W;
+// launch_rownorm_repair, enqueued right after, writes those tiles.
 hipError_t launch_rownorm_tall(hipStream_t s, const MatDev* mats, const TileItem* tiles,
-                               int64_t ntiles, TallSync* sync, uint32_t* giveups,
-                               StepScalars sc);
+                               int64_t ntiles, TallSync* sync, TallCtl* ctl, uint32_t* repair,
+                               uint32_t poll_limit, StepScalars sc);
+hipError_t launch_rownorm_repair(hipStream_t s, const MatDev* mats, const TileItem* tiles,
+                                 int64_t ntiles, TallCtl* ctl, const uint32_t* repair,
+                                 StepScalars sc);
 // Workgroups of the single-pass tall kernel that fit on one CU at once.
 hipError_t rownorm_tall_resident(int* workgroups_per_cu);
 // Refresh prep: momentum, Frobenius partials, unscaled X0 in both layouts.
@@ -149,6 +167,7 @@ constexpr int kColTileCols = 256;      // tall RowNorm tile columns
 constexpr int kTallRows = 256;         // single-pass tall RowNorm tile rows
 constexpr int kTallCols = 128;         // single-pass tall RowNorm strip width
 constexpr int kTallMaxChunks = 128;    // single pass only for rows <= 128 * 256
+constexpr uint32_t kTallPollLimit = 1u << 18;   // default polls before a wait gives up
 constexpr int kPrepTile = 64;          // NS5 cast/transpose tile
 constexpr int kAdamChunk = 4096;       // elements per AdamW workgroup
 

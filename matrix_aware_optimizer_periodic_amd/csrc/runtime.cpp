@@ -73,7 +73,7 @@ struct Plan {
   std::vector<AdamChunk> adam_chunks;
   std::vector<NsChunk> ns_full, ns_block;
   size_t off_mats = 0, off_adams = 0, off_col_tiles = 0, off_col_strips = 0, off_adam_chunks = 0;
-  size_t off_tall_tiles = 0, off_tall_sync = 0, tall_sync_bytes = 0;
+  size_t off_tall_tiles = 0, off_tall_sync = 0, tall_sync_bytes = 0, tall_list_bytes = 0;
   size_t ws_base = 0, ws_bytes = 0;
   size_t zero_end = 0;                    // bytes [0, zero_end) are zeroed at init
   size_t total = 0;
@@ -289,9 +289,13 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
 // its workgroups the device holds at once.  Table and buffer sizes are
 // reserved for every eligible matrix either way, so the state size does not
 // depend on it.
+//
+// ext_mom: when given (the no-alloc entry point), the momentum of matrix i is
+// the caller's ext_mom[i] instead of a region of the buffer.
 muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const int32_t* kinds,
                        int32_t n, char* base, Plan& pl, std::string& err,
-                       int64_t tall_limit = kTallMaxChunks) {
+                       int64_t tall_limit = kTallMaxChunks,
+                       const muon_tensor* ext_mom = nullptr) {
   pl = Plan();
   Bump bump;
   pl.table_index.assign(n, -1);
@@ -302,7 +306,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
     const size_t numel = size_t(t.rows) * size_t(t.cols);
     if (kinds[i] == MUON_KIND_MATRIX) {
       pl.table_index[i] = static_cast<int32_t>(pl.mats.size());
-      pl.mom_off[i] = bump.take(numel * 4);
+      if (!ext_mom) pl.mom_off[i] = bump.take(numel * 4);
       MatDev d{};
       d.rows = t.rows; d.cols = t.cols;
       pl.mats.push_back(d);
@@ -315,8 +319,8 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
       pl.adams.push_back(a);
     }
   }
-  pl.zero_end = bump.cur;
-  // 2. RowNorm plan
+  // 2. RowNorm plan (its partial rows are zeroed at init with the state, so
+  //    no launch ever reads a value no kernel wrote)
   const bool cols_mode = cfg.rownorm_axis == 0;
   std::vector<RowGroup> groups(7);
   const int classes[7] = {0, 1, 2, 4, 8, 16, 32};
@@ -366,6 +370,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
       g.prefix.push_back(g.prefix.back() + t.rows);
     }
   }
+  pl.zero_end = bump.cur;
   for (RowGroup& g : groups)
     if (!g.ids.empty()) pl.row_groups.push_back(std::move(g));
   // 3. AdamW chunks
@@ -417,8 +422,12 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
   pl.off_col_tiles = bump.take(size_t(pl.n_col_tiles_max) * sizeof(TileItem));
   pl.off_col_strips = bump.take(size_t(pl.n_col_strips_max) * sizeof(TileItem));
   pl.off_tall_tiles = bump.take(size_t(pl.n_tall_tiles_max) * sizeof(TileItem));
-  // give-up count (word 1 of 16 B), then one TallSync per strip
-  pl.tall_sync_bytes = pl.n_tall_tiles_max ? 16 + size_t(pl.n_tall_sync_max) * sizeof(TallSync) : 0;
+  // the control line, the repair list (one word per tile), then one
+  // TallSync per strip
+  pl.tall_list_bytes = align_up(size_t(pl.n_tall_tiles_max) * 4, sizeof(TallSync));
+  pl.tall_sync_bytes = pl.n_tall_tiles_max ? sizeof(TallCtl) + pl.tall_list_bytes +
+                                                 size_t(pl.n_tall_sync_max) * sizeof(TallSync)
+                                           : 0;
   pl.off_tall_sync = bump.take(pl.tall_sync_bytes);
   pl.off_adam_chunks = bump.take(pl.adam_chunks.size() * sizeof(AdamChunk));
   for (RowGroup& g : pl.row_groups) {
@@ -446,7 +455,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
     const int32_t k = pl.table_index[i];
     if (kinds[i] == MUON_KIND_MATRIX) {
       MatDev& d = pl.mats[k];
-      d.mom = static_cast<float*>(at(pl.mom_off[i]));
+      d.mom = ext_mom ? static_cast<float*>(ext_mom[i].ptr) : static_cast<float*>(at(pl.mom_off[i]));
       d.part = static_cast<float*>(at(pl.part_off[i]));
     } else {
       AdamDev& a = pl.adams[k];
@@ -523,6 +532,7 @@ struct muon_ctx {
   Plan plan;
   std::string err;
   bool broken = false;
+  uint32_t poll_limit = kTallPollLimit;   // single-pass tall RowNorm waits
   // measurement hook
   bool timing = false;
   std::vector<hipEvent_t> events;            // pool, two per recorded launch
@@ -543,10 +553,38 @@ muon_status hip_fail(muon_ctx* ctx, hipError_t e, const char* what) {
 }
 
 template <typename T>
-hipError_t upload(muon_ctx* ctx, size_t off, const std::vector<T>& v) {
+hipError_t upload(hipStream_t s, char* base, size_t off, const std::vector<T>& v) {
   if (v.empty()) return hipSuccess;
-  return hipMemcpyAsync(ctx->base + off, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice,
-                        ctx->stream);
+  return hipMemcpyAsync(base + off, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice, s);
+}
+
+// Enqueue the copies of every launch table of pl to base + its offsets.  The
+// host vectors must stay alive until the stream has passed the copies.
+hipError_t upload_plan(hipStream_t s, char* base, const Plan& pl, const char** what) {
+  *what = "hipMemcpyAsync(tables)";
+  hipError_t e = hipSuccess;
+  auto up = [&](size_t off, const auto& v) {
+    if (e == hipSuccess) e = upload(s, base, off, v);
+  };
+  up(pl.off_mats, pl.mats);
+  up(pl.off_adams, pl.adams);
+  up(pl.off_col_tiles, pl.col_tiles);
+  up(pl.off_col_strips, pl.col_strips);
+  up(pl.off_tall_tiles, pl.tall_tiles);
+  up(pl.off_adam_chunks, pl.adam_chunks);
+  for (const RowGroup& g : pl.row_groups) {
+    up(g.off_ids, g.ids);
+    up(g.off_prefix, g.prefix);
+  }
+  for (const auto* plan : {&pl.ns_full, &pl.ns_block})
+    for (const NsChunk& ch : *plan) {
+      up(ch.off_ns, ch.ns);
+      up(ch.off_prep, ch.prep_items);
+      for (const auto& op : ch.gemm)
+        for (const auto& gl : op) up(gl.off, gl.items);
+      up(ch.prod_wide.off, ch.prod_wide.items);
+    }
+  return e;
 }
 
 // Records a start event for kernel class cls when timing is on; close()
@@ -611,6 +649,111 @@ muon_status run_ns(muon_ctx* ctx, std::vector<NsChunk>& chunks) {
                                                   c.muon_wd)));
         }
     }
+  }
+  return MUON_OK;
+}
+
+// The caller's weights and gradients in the plan's tables (build_plan fills
+// everything else).
+void bind_tensors(Plan& pl, const muon_tensor* params, const muon_tensor* grads,
+                  const int32_t* kinds, int32_t n) {
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t k = pl.table_index[i];
+    if (kinds[i] == MUON_KIND_MATRIX) {
+      pl.mats[k].w = static_cast<float*>(params[i].ptr);
+      pl.mats[k].g = grads[i].ptr;
+      pl.mats[k].gdt = grads[i].dtype;
+    } else {
+      pl.adams[k].p = static_cast<float*>(params[i].ptr);
+      pl.adams[k].g = grads[i].ptr;
+      pl.adams[k].gdt = grads[i].dtype;
+    }
+  }
+}
+
+// The single-pass tall RowNorm kernel needs every workgroup of a column
+// strip resident at once; strips of up to half the current device's
+// capacity (so up to half of each XCD's, as a strip's workgroups are dealt
+// round-robin to the XCDs) take it, the rest the two-pass kernels.  0 when
+// the device cannot be queried.
+int64_t device_tall_limit() {
+  int dev = 0, cus = 0, per_cu = 0;
+  int64_t lim = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      rownorm_tall_resident(&per_cu) == hipSuccess)
+    lim = std::min<int64_t>(kTallMaxChunks, int64_t(cus) * per_cu / 2);
+  (void)hipGetLastError();
+  return lim;
+}
+
+// The launches of one step t on ctx's stream, from its plan: the branch's
+// kernels over every matrix, then AdamW over the other tensors.
+muon_status enqueue_step(muon_ctx* ctx, int64_t step) {
+  Plan& pl = ctx->plan;
+  // Host copies of the tables: every tensor pointer must be bound before a
+  // kernel may use it.
+  for (const MatDev& d : pl.mats)
+    if (!d.w || !d.g || !d.mom) { ctx->err = "internal: unbound matrix tensor"; return MUON_E_STATE; }
+  for (const AdamDev& a : pl.adams)
+    if (!a.p || !a.g) { ctx->err = "internal: unbound AdamW tensor"; return MUON_E_STATE; }
+  MatDev* mats = reinterpret_cast<MatDev*>(ctx->base + pl.off_mats);
+  AdamDev* adams = reinterpret_cast<AdamDev*>(ctx->base + pl.off_adams);
+  const muon_config& c = ctx->cfg;
+  const int32_t br = muon_branch(&c, step);
+  muon_status st = MUON_OK;
+  if (!pl.mats.empty()) {
+    if (br == MUON_BRANCH_ROWNORM) {
+      StepScalars sc{c.lr, c.beta, c.gamma, c.eps_row, c.muon_wd};
+      for (RowGroup& g : pl.row_groups) {
+        const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_ROWS, launch_rownorm_rows(
+            ctx->stream, mats, reinterpret_cast<const int32_t*>(ctx->base + g.off_ids),
+            reinterpret_cast<const int64_t*>(ctx->base + g.off_prefix), int32_t(g.ids.size()),
+            g.prefix.back(), g.max_chunks, sc));
+        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_rows"); }
+      }
+      if (!pl.tall_tiles.empty()) {
+        char* tb = ctx->base + pl.off_tall_sync;
+        TallCtl* ctl = reinterpret_cast<TallCtl*>(tb);
+        uint32_t* list = reinterpret_cast<uint32_t*>(tb + sizeof(TallCtl));
+        TallSync* sync = reinterpret_cast<TallSync*>(tb + sizeof(TallCtl) + pl.tall_list_bytes);
+        const TileItem* tt = reinterpret_cast<const TileItem*>(ctx->base + pl.off_tall_tiles);
+        const int64_t nt = int64_t(pl.tall_tiles.size());
+        hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_TALL, launch_rownorm_tall(
+            ctx->stream, mats, tt, nt, sync, ctl, list, ctx->poll_limit, sc));
+        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_tall"); }
+        e = MUON_TIMED(ctx, MUON_K_ROWNORM_REPAIR,
+                       launch_rownorm_repair(ctx->stream, mats, tt, nt, ctl, list, sc));
+        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_repair"); }
+      }
+      const TileItem* tiles = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_tiles);
+      const TileItem* strips = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_strips);
+      for (int phase = 1; phase <= 2 && !pl.col_tiles.empty(); ++phase) {
+        if (phase == 2) {
+          const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_COEF,
+                                          launch_rownorm_coef(ctx->stream, mats, strips,
+                                                              int64_t(pl.col_strips.size()), sc));
+          if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_coef"); }
+        }
+        const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_COLS1 + phase - 1,
+                                        launch_rownorm_cols(ctx->stream, mats, tiles,
+                                                            int64_t(pl.col_tiles.size()), phase, sc));
+        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_cols"); }
+      }
+    } else {
+      st = run_ns(ctx, br == MUON_BRANCH_NS5 ? pl.ns_full : pl.ns_block);
+      if (st != MUON_OK) { ctx->broken = true; return st; }
+    }
+  }
+  if (!pl.adams.empty()) {
+    const double n1 = double(step) + 1.0;
+    const float bc1 = float(1.0 - std::pow(double(c.adam_b1), n1));
+    const float bc2 = float(1.0 - std::pow(double(c.adam_b2), n1));
+    const hipError_t e = MUON_TIMED(ctx, MUON_K_ADAMW, launch_adamw(
+        ctx->stream, adams, reinterpret_cast<const AdamChunk*>(ctx->base + pl.off_adam_chunks),
+        int64_t(pl.adam_chunks.size()), c.adam_lr, c.adam_b1, c.adam_b2, c.adam_eps, c.adam_wd,
+        bc1, bc2));
+    if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "adamw"); }
   }
   return MUON_OK;
 }
@@ -689,73 +832,25 @@ muon_status muon_init(muon_ctx** out, const muon_config* cfg, const muon_tensor*
   ctx->params.assign(params, params + n);
   ctx->grads.assign(grads, grads + n);
   ctx->kinds.assign(kinds, kinds + n);
-  // The single-pass tall RowNorm kernel needs every workgroup of a column
-  // strip resident at once; strips of up to half the device's capacity (so
-  // up to half of each XCD's, as a strip's workgroups are dealt round-robin
-  // to the XCDs) take it, the rest the two-pass kernels.
-  int64_t tall_limit = 0;
-  if (probe.n_tall_tiles_max > 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        rownorm_tall_resident(&per_cu) == hipSuccess)
-      tall_limit = std::min<int64_t>(kTallMaxChunks, int64_t(cus) * per_cu / 2);
-    (void)hipGetLastError();
-  }
+  const int64_t tall_limit = probe.n_tall_tiles_max > 0 ? device_tall_limit() : 0;
   build_plan(*cfg, params, kinds, n, ctx->base, ctx->plan, err, tall_limit);
   Plan& pl = ctx->plan;
-  for (int32_t i = 0; i < n; ++i) {
-    const int32_t k = pl.table_index[i];
-    if (kinds[i] == MUON_KIND_MATRIX) {
-      pl.mats[k].w = static_cast<float*>(params[i].ptr);
-      pl.mats[k].g = grads[i].ptr;
-      pl.mats[k].gdt = grads[i].dtype;
-    } else {
-      pl.adams[k].p = static_cast<float*>(params[i].ptr);
-      pl.adams[k].g = grads[i].ptr;
-      pl.adams[k].gdt = grads[i].dtype;
-    }
-  }
-  auto fail = [&](hipError_t e, const char* what) {
+  bind_tensors(pl, params, grads, kinds, n);
+  hipError_t e = hipGetDevice(&ctx->device);
+  if (e == hipSuccess && pl.zero_end) e = hipMemsetAsync(ctx->base, 0, pl.zero_end, ctx->stream);
+  if (e == hipSuccess && pl.tall_sync_bytes)
+    e = hipMemsetAsync(ctx->base + pl.off_tall_sync, 0, pl.tall_sync_bytes, ctx->stream);
+  const char* what = "muon_init: zeroing the state";
+  if (e == hipSuccess) e = upload_plan(ctx->stream, ctx->base, pl, &what);
+  // The host copies of the tables must outlive the transfers.
+  if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) {
     char buf[256];
     snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
     g_last_error = buf;
     delete ctx;
     return MUON_E_HIP;
-  };
-  hipError_t e = hipGetDevice(&ctx->device);
-  if (e != hipSuccess) return fail(e, "hipGetDevice");
-  if (pl.zero_end) {
-    e = hipMemsetAsync(ctx->base, 0, pl.zero_end, ctx->stream);
-    if (e != hipSuccess) return fail(e, "hipMemsetAsync(state)");
   }
-  if (pl.tall_sync_bytes) {
-    e = hipMemsetAsync(ctx->base + pl.off_tall_sync, 0, pl.tall_sync_bytes, ctx->stream);
-    if (e != hipSuccess) return fail(e, "hipMemsetAsync(tall sync)");
-  }
-  const hipError_t ups[] = {
-      upload(ctx, pl.off_mats, pl.mats), upload(ctx, pl.off_adams, pl.adams),
-      upload(ctx, pl.off_col_tiles, pl.col_tiles), upload(ctx, pl.off_col_strips, pl.col_strips),
-      upload(ctx, pl.off_tall_tiles, pl.tall_tiles),
-      upload(ctx, pl.off_adam_chunks, pl.adam_chunks)};
-  for (hipError_t u : ups)
-    if (u != hipSuccess) return fail(u, "hipMemcpyAsync(tables)");
-  for (RowGroup& g : pl.row_groups) {
-    if ((e = upload(ctx, g.off_ids, g.ids)) != hipSuccess) return fail(e, "hipMemcpyAsync(rows)");
-    if ((e = upload(ctx, g.off_prefix, g.prefix)) != hipSuccess) return fail(e, "hipMemcpyAsync(rows)");
-  }
-  for (auto* plan : {&pl.ns_full, &pl.ns_block})
-    for (NsChunk& ch : *plan) {
-      if ((e = upload(ctx, ch.off_ns, ch.ns)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
-      if ((e = upload(ctx, ch.off_prep, ch.prep_items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
-      for (auto& op : ch.gemm)
-        for (auto& gl : op)
-          if ((e = upload(ctx, gl.off, gl.items)) != hipSuccess) return fail(e, "hipMemcpyAsync(ns)");
-      if ((e = upload(ctx, ch.prod_wide.off, ch.prod_wide.items)) != hipSuccess)
-        return fail(e, "hipMemcpyAsync(ns)");
-    }
-  // The host copies of the tables must outlive the transfers.
-  if ((e = hipStreamSynchronize(ctx->stream)) != hipSuccess) return fail(e, "hipStreamSynchronize");
   *out = ctx;
   return MUON_OK;
 }
@@ -816,56 +911,7 @@ muon_status muon_step(muon_ctx* ctx, const muon_tensor* params, const muon_tenso
     if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "patch"); }
   }
 
-  const muon_config& c = ctx->cfg;
-  const int32_t br = muon_branch(&c, step);
-  muon_status st = MUON_OK;
-  if (!pl.mats.empty()) {
-    if (br == MUON_BRANCH_ROWNORM) {
-      StepScalars sc{c.lr, c.beta, c.gamma, c.eps_row, c.muon_wd};
-      for (RowGroup& g : pl.row_groups) {
-        const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_ROWS, launch_rownorm_rows(
-            ctx->stream, mats, reinterpret_cast<const int32_t*>(ctx->base + g.off_ids),
-            reinterpret_cast<const int64_t*>(ctx->base + g.off_prefix), int32_t(g.ids.size()),
-            g.prefix.back(), g.max_chunks, sc));
-        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_rows"); }
-      }
-      if (!pl.tall_tiles.empty()) {
-        uint32_t* ctl = reinterpret_cast<uint32_t*>(ctx->base + pl.off_tall_sync);
-        const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_TALL, launch_rownorm_tall(
-            ctx->stream, mats, reinterpret_cast<const TileItem*>(ctx->base + pl.off_tall_tiles),
-            int64_t(pl.tall_tiles.size()), reinterpret_cast<TallSync*>(ctl + 4), ctl + 1, sc));
-        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_tall"); }
-      }
-      const TileItem* tiles = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_tiles);
-      const TileItem* strips = reinterpret_cast<const TileItem*>(ctx->base + pl.off_col_strips);
-      for (int phase = 1; phase <= 2 && !pl.col_tiles.empty(); ++phase) {
-        if (phase == 2) {
-          const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_COEF,
-                                          launch_rownorm_coef(ctx->stream, mats, strips,
-                                                              int64_t(pl.col_strips.size()), sc));
-          if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_coef"); }
-        }
-        const hipError_t e = MUON_TIMED(ctx, MUON_K_ROWNORM_COLS1 + phase - 1,
-                                        launch_rownorm_cols(ctx->stream, mats, tiles,
-                                                            int64_t(pl.col_tiles.size()), phase, sc));
-        if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "rownorm_cols"); }
-      }
-    } else {
-      st = run_ns(ctx, br == MUON_BRANCH_NS5 ? pl.ns_full : pl.ns_block);
-      if (st != MUON_OK) { ctx->broken = true; return st; }
-    }
-  }
-  if (!pl.adams.empty()) {
-    const double n1 = double(step) + 1.0;
-    const float bc1 = float(1.0 - std::pow(double(c.adam_b1), n1));
-    const float bc2 = float(1.0 - std::pow(double(c.adam_b2), n1));
-    const hipError_t e = MUON_TIMED(ctx, MUON_K_ADAMW, launch_adamw(
-        ctx->stream, adams, reinterpret_cast<const AdamChunk*>(ctx->base + pl.off_adam_chunks),
-        int64_t(pl.adam_chunks.size()), c.adam_lr, c.adam_b1, c.adam_b2, c.adam_eps, c.adam_wd,
-        bc1, bc2));
-    if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "adamw"); }
-  }
-  return MUON_OK;
+  return enqueue_step(ctx, step);
 }
 
 muon_status muon_state(const muon_ctx* ctx, int32_t i, int32_t which, muon_tensor* view) {
@@ -926,19 +972,28 @@ muon_status muon_timing_read(muon_ctx* ctx, double* ms, int64_t* launches) {
 
 muon_status muon_sync(muon_ctx* ctx) {
   if (!ctx) return MUON_E_ARG;
-  hipError_t e = hipStreamSynchronize(ctx->stream);
+  const hipError_t e = hipStreamSynchronize(ctx->stream);
   if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "muon_sync"); }
+  return MUON_OK;
+}
+
+muon_status muon_tall_poll_limit(muon_ctx* ctx, uint32_t polls) {
+  if (!ctx) return MUON_E_ARG;
+  ctx->poll_limit = polls;
+  return MUON_OK;
+}
+
+muon_status muon_tall_giveups(muon_ctx* ctx, uint64_t* count) {
+  if (!ctx || !count) return MUON_E_ARG;
+  *count = 0;
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "muon_tall_giveups"); }
   const Plan& pl = ctx->plan;
-  if (pl.tall_sync_bytes) {
-    uint32_t ctl[2] = {0, 0};
-    e = hipMemcpy(ctl, ctx->base + pl.off_tall_sync, sizeof ctl, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "muon_sync"); }
-    if (ctl[1] != 0) {
-      ctx->err = std::to_string(ctl[1]) +
-                 " single-pass tall RowNorm workgroup(s) stopped waiting for their column strip";
-      return MUON_E_STATE;
-    }
-  }
+  if (!pl.tall_sync_bytes) return MUON_OK;
+  TallCtl ctl{};
+  e = hipMemcpy(&ctl, ctx->base + pl.off_tall_sync, sizeof ctl, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) { ctx->broken = true; return hip_fail(ctx, e, "muon_tall_giveups"); }
+  *count = ctl.giveups;
   return MUON_OK;
 }
 

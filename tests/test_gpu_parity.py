@@ -191,8 +191,55 @@ def test_tall_rownorm_single_and_two_pass(single, grad_dtype):
         rec = m.muon_timing_read(sess.ctx)
         assert (rec["rownorm_tall"][1] > 0) == bool(single)
         assert (rec["rownorm_cols1"][1] > 0) == (not single)
+        assert sess.tall_giveups() == 0
     finally:
         sess.close()
+
+
+def test_tall_single_pass_forced_giveups_are_repaired():
+    """With a poll limit of 0, every workgroup of the single-pass tall
+    RowNorm that does not itself complete its strip stops waiting at once:
+    it must leave its tile of W alone and list it, and the repair launch
+    must write it.  W then matches the oracle on the same ragged and DiT
+    shapes as above, and equals a run at the default limit bit for bit
+    (same arithmetic, whichever launch writes a tile).  The limit is set from
+    the host, so every kernel still exits normally."""
+    m = _lib()
+    shapes = [(1000, 300), (129, 4), (4096, 1024), (32768, 256), (2200, 2048), (6144, 2048)]
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    G = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    sess = m.MuonSession(W, G, kinds=[m.MUON_KIND_MATRIX] * len(shapes))
+    try:
+        m.muon_tall_poll_limit(sess.ctx, 0)
+        m.muon_timing_enable(sess.ctx, True)
+        _direction_loop(sess, shapes, 3, W, G, torch.bfloat16, "bf16", 1e-3, 12, None)
+        rec = m.muon_timing_read(sess.ctx)
+        gave = sess.tall_giveups()
+        print(f"waits that gave up and were repaired: {gave}", flush=True)
+        assert rec["rownorm_tall"][1] == 2 and rec["rownorm_repair"][1] == 2
+        assert gave > 0
+    finally:
+        sess.close()
+    out = {}
+    for limit in (0, None):
+        Wb = [torch.from_numpy(workloads.host_weight0(5, i, s)).cuda() for i, s in enumerate(shapes)]
+        Gb = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+        sb = m.MuonSession(Wb, Gb, kinds=[m.MUON_KIND_MATRIX] * len(shapes), K=1000)
+        try:
+            if limit is not None:
+                m.muon_tall_poll_limit(sb.ctx, limit)
+            for t in range(1, 6):
+                for i, s in enumerate(shapes):
+                    Gb[i].copy_(torch.from_numpy(workloads.host_grad(5, t, i, s, 1e-3, "bf16")).to(
+                        torch.bfloat16))
+                sb.step(t)
+            gave = sb.tall_giveups()
+            assert (gave > 0) == (limit == 0), gave
+            out[limit] = [w.clone() for w in Wb] + [sb.state_view(i).clone() for i in range(len(shapes))]
+        finally:
+            sb.close()
+    for a, b in zip(out[0], out[None]):
+        assert torch.equal(a, b)
 
 
 def test_tall_single_pass_with_two_pass_fallback():
@@ -233,7 +280,7 @@ def test_tall_single_pass_repeated_launches():
         try:
             for t in range(1, 21):
                 sess.step(t)
-            sess.sync()
+            assert sess.tall_giveups() == 0
             out[single] = [w.double().cpu().numpy() for w in W]
         finally:
             sess.close()
@@ -511,7 +558,7 @@ def test_dit_full_set_sampled(name):
                 workloads.device_normal_(grads[i], wl.grad_std, workloads.seed_for(0, t, i, 1))
                 params[i].zero_()
             sess.step(t)
-            sess.sync()                  # also: no cross-workgroup wait gave up
+            sess.sync()
             br = sess.branch(t)
             assert br == oracle.branch(t, ocfg)
             lr = ocfg.lr * (ocfg.bp_lr_ratio if br == oracle.BRANCH_BLOCK_NS5 else 1.0)
@@ -562,6 +609,8 @@ def test_dit_full_set_sampled(name):
                     del S, X, Uw
                 print(f"{name} t={t} NS5: worst asymmetry of X U^T / its bound {worst:.2e}",
                       flush=True)
+        # the residency bound holds on an otherwise idle device: no wait gave up
+        assert sess.tall_giveups() == 0
     finally:
         sess.close()
         del params, grads
