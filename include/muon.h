@@ -186,6 +186,30 @@ muon_status muon_init(muon_ctx** out, const muon_config* cfg,
 muon_status muon_step(muon_ctx* ctx, const muon_tensor* params,
                       const muon_tensor* grads, int64_t step);
 
+/* For callers that cannot allocate device memory (serving loops, harnesses
+ * that forbid hipMalloc): one optimizer step of n Muon matrices, like
+ * muon_step, with no context and no state buffer.  The caller passes each
+ * matrix's weight (params[i], F32), gradient (grads[i], F32 or BF16) and
+ * momentum (moms[i], F32, same shape; read and written, zero before the
+ * first step).  Everything else the step needs - launch tables, the
+ * Newton-Schulz workspace, RowNorm column partials and counters - lives in
+ * one static device array of 128 MiB per GPU (held from the library's first
+ * use on that GPU until the process ends).  The call allocates nothing: it
+ * clears the array's counters with a kernel, copies the launch tables into
+ * it, waits for hip_stream once (so it cannot be captured into a graph),
+ * then enqueues the step.  Matrices are planned in chunks whose workspace
+ * fits the array; a step whose largest matrix does not fit (bf16
+ * workspace about 2 (2 r c + 2 r^2) bytes, r x c the padded short x long
+ * side: e.g. 2048 x 12288 fits, 3072 x 18432 does not) returns
+ * MUON_E_WORKSPACE with the size it needed, having enqueued nothing.  Every
+ * call on a GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other host threads, or other
+ * streams not yet past an earlier call) race and give wrong results.
+ * Other errors as muon_step; muon_last_error(NULL) gives the text. */
+muon_status muon_step_noalloc(const muon_config* cfg, const muon_tensor* params,
+                              const muon_tensor* grads, const muon_tensor* moms, int32_t n,
+                              int64_t step, void* hip_stream);
+
 /* A view into the state buffer, for checkpointing and inspection.  Source:
  * "Scaling Muon for Diffusion Transformers", English abstract (the momentum
  * is stored explicitly and in full, so it can be read back and restored).

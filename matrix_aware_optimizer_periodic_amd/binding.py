@@ -24,7 +24,7 @@ MUON_NS_BF16, MUON_NS_F32 = 0, 1
 EXPORTED = ("muon_config_default", "muon_state_bytes", "muon_init", "muon_step", "muon_state",
             "muon_branch", "muon_free", "muon_status_str", "muon_last_error",
             "muon_timing_enable", "muon_timing_read", "muon_sync", "muon_tall_poll_limit",
-            "muon_tall_giveups")
+            "muon_tall_giveups", "muon_step_noalloc")
 
 # muon_kernel_class, in enum order
 KERNEL_CLASSES = ("rownorm_rows", "rownorm_cols1", "rownorm_cols2", "ns_prep", "ns_scale",
@@ -125,6 +125,10 @@ def lib() -> ctypes.CDLL:
         L.muon_tall_poll_limit.restype = ctypes.c_int
         L.muon_tall_giveups.argtypes = [ctypes.c_void_p, P(ctypes.c_uint64)]
         L.muon_tall_giveups.restype = ctypes.c_int
+        L.muon_step_noalloc.argtypes = [P(MuonConfig), P(MuonTensor), P(MuonTensor),
+                                        P(MuonTensor), ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_void_p]
+        L.muon_step_noalloc.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -230,6 +234,13 @@ def muon_timing_read(ctx) -> dict:
 def muon_sync(ctx) -> None:
     """Wait for the context's stream; raises MuonError if the wait failed."""
     _check(lib().muon_sync(ctx), ctx)
+
+
+def muon_step_noalloc(cfg: MuonConfig, params, grads, moms, step: int, stream: int = 0) -> None:
+    n = len(params)
+    _check(lib().muon_step_noalloc(ctypes.byref(cfg), _array(MuonTensor, params),
+                                   _array(MuonTensor, grads), _array(MuonTensor, moms), n, step,
+                                   ctypes.c_void_p(stream)))
 
 
 def muon_tall_poll_limit(ctx, polls: int) -> None:

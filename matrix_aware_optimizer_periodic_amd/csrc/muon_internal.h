@@ -158,6 +158,12 @@ hipError_t launch_adamw(hipStream_t s, const AdamDev* t, const AdamChunk* chunks
                         int64_t nchunks, float lr, float b1, float b2, float eps,
                         float wd, float bc1, float bc2);
 hipError_t launch_patch(hipStream_t s, MatDev* mats, AdamDev* adams, const PatchArgs& args);
+// Zero `bytes` (a multiple of 4) at the device address p with a kernel (no
+// memset node, so a captured launch replays it unchanged).
+hipError_t launch_fill_zero(hipStream_t s, void* p, size_t bytes);
+// Device address of the no-alloc scratch array on the current device
+// (kNoallocScratchBytes bytes), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
 
 constexpr int kGemmGram = 0, kGemmPoly = 1, kGemmProduct = 2;
 constexpr int kGemmProductLast = 3;  // kernel variant only: product that updates W
@@ -170,5 +176,6 @@ constexpr int kTallMaxChunks = 128;    // single pass only for rows <= 128 * 256
 constexpr uint32_t kTallPollLimit = 1u << 18;   // default polls before a wait gives up
 constexpr int kPrepTile = 64;          // NS5 cast/transpose tile
 constexpr int kAdamChunk = 4096;       // elements per AdamW workgroup
+constexpr size_t kNoallocScratchBytes = size_t(128) << 20;   // muon_step_noalloc scratch
 
 }  // namespace muon

@@ -997,6 +997,88 @@ muon_status muon_tall_giveups(muon_ctx* ctx, uint64_t* count) {
   return MUON_OK;
 }
 
+muon_status muon_step_noalloc(const muon_config* cfg, const muon_tensor* params,
+                              const muon_tensor* grads, const muon_tensor* moms, int32_t n,
+                              int64_t step, void* hip_stream) {
+  std::string err;
+  if (step < 0) { g_last_error = "step must be >= 0"; return MUON_E_ARG; }
+  if (n > 0 && !moms) { g_last_error = "moms is NULL"; return MUON_E_ARG; }
+  std::vector<int32_t> kinds(size_t(std::max(n, 0)), MUON_KIND_MATRIX);
+  muon_status st = validate_list(cfg, params, grads, kinds.data(), n, true, err);
+  if (st != MUON_OK) { g_last_error = err; return st; }
+  for (int32_t i = 0; i < n; ++i) {
+    if ((st = check_tensor(moms[i], true, "momentum", i, err)) != MUON_OK ||
+        (st = check_ptr(moms[i].ptr, "momentum", i, err)) != MUON_OK) {
+      g_last_error = err;
+      return st;
+    }
+    if (moms[i].rows != params[i].rows || moms[i].cols != params[i].cols) {
+      g_last_error = "momentum " + std::to_string(i) + ": shape differs from its param";
+      return MUON_E_SHAPE;
+    }
+  }
+  if (n == 0) return MUON_OK;
+  // Plan into the scratch array: tables, partials and counters first, then
+  // the Newton-Schulz workspace of one chunk, its cap set to what is left.
+  Plan probe;
+  st = build_plan(*cfg, params, kinds.data(), n, nullptr, probe, err, kTallMaxChunks, moms);
+  if (st != MUON_OK) { g_last_error = err; return st; }
+  void* sp = nullptr;
+  hipError_t e = noalloc_scratch(&sp);
+  if (e != hipSuccess) {
+    g_last_error = std::string("muon_step_noalloc: scratch address: ") + hipGetErrorString(e);
+    return MUON_E_HIP;
+  }
+  const int64_t tall_limit = probe.n_tall_tiles_max > 0 ? device_tall_limit() : 0;
+  muon_config c = *cfg;
+  Plan pl;
+  size_t cap = kNoallocScratchBytes;
+  for (int attempt = 0; attempt < 4; ++attempt) {
+    c.ns_workspace_max = cfg->ns_workspace_max ? std::min<uint64_t>(cfg->ns_workspace_max, cap) : cap;
+    st = build_plan(c, params, kinds.data(), n, static_cast<char*>(sp), pl, err, tall_limit, moms);
+    if (st != MUON_OK) { g_last_error = err; return st; }
+    const size_t other = pl.total - pl.ws_bytes;
+    if (pl.total <= kNoallocScratchBytes || other + kAlign >= kNoallocScratchBytes) break;
+    cap = kNoallocScratchBytes - other - kAlign;
+  }
+  if (pl.total > kNoallocScratchBytes) {
+    g_last_error = "muon_step_noalloc: this step needs " + std::to_string(pl.total) +
+                   " bytes of device scratch (launch tables, partial sums and the largest "
+                   "matrix's Newton-Schulz workspace); the array holds " +
+                   std::to_string(kNoallocScratchBytes);
+    return MUON_E_WORKSPACE;
+  }
+  bind_tensors(pl, params, grads, kinds.data(), n);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char* base = static_cast<char*>(sp);
+  const char* what = "muon_step_noalloc: clearing the scratch counters";
+  // The array keeps the last call's contents: clear the partial rows and the
+  // tall RowNorm counters, which must start at zero.
+  e = launch_fill_zero(s, base, pl.zero_end);
+  if (e == hipSuccess && pl.tall_sync_bytes)
+    e = launch_fill_zero(s, base + pl.off_tall_sync, pl.tall_sync_bytes);
+  if (e == hipSuccess) e = upload_plan(s, base, pl, &what);
+  // The host copies of the tables must outlive the transfers.
+  if (e == hipSuccess) {
+    what = "muon_step_noalloc: hipStreamSynchronize";
+    e = hipStreamSynchronize(s);
+  }
+  if (e != hipSuccess) {
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return MUON_E_HIP;
+  }
+  muon_ctx tmp;
+  tmp.cfg = c;
+  tmp.stream = s;
+  tmp.base = base;
+  tmp.n = n;
+  tmp.plan = std::move(pl);
+  (void)hipGetDevice(&tmp.device);
+  st = enqueue_step(&tmp, step);
+  if (st != MUON_OK) g_last_error = tmp.err;
+  return st;
+}
+
 void muon_free(muon_ctx* ctx) { delete ctx; }
 
 const char* muon_status_str(int32_t s) {

@@ -207,6 +207,13 @@ void check_adam(const muon::AdamDev* t, const muon::AdamChunk* chunks, int64_t n
   }
 }
 
+// ---- no-alloc scratch stand-in --------------------------------------------
+void* scratch_buffer() {
+  static void* p = nullptr;
+  if (!p) p = std::aligned_alloc(256, muon::kNoallocScratchBytes);
+  return p;
+}
+
 }  // namespace chk
 
 // ---- stubbed HIP runtime --------------------------------------------------
@@ -241,6 +248,14 @@ hipError_t hipEventDestroy(hipEvent_t e) { delete reinterpret_cast<int*>(e); ret
 // ---- stubbed launchers (muon_internal.h) -----------------------------------
 namespace muon {
 hipError_t rownorm_tall_resident(int* w) { *w = 2; return hipSuccess; }
+hipError_t noalloc_scratch(void** p) { *p = chk::scratch_buffer(); return hipSuccess; }
+hipError_t launch_fill_zero(hipStream_t, void* p, size_t bytes) {
+  ++chk::g_launches;
+  if (bytes % 4) chk::fail("fill_zero: %zu bytes", bytes);
+  chk::need(p, double(bytes), "fill_zero");
+  if (!chk::g_fail) std::memset(p, 0, bytes);
+  return hipSuccess;
+}
 hipError_t launch_rownorm_rows(hipStream_t, const MatDev* mats, const int32_t* ids,
                                const int64_t* prefix, int32_t nmat, int64_t total_rows,
                                int max_chunks, StepScalars) {
@@ -544,9 +559,10 @@ void fill(void* p, size_t floats, uint32_t seed) {
 }
 
 void full(const char* name, const std::vector<std::pair<int64_t, int64_t>>& shapes, int n_adam,
-          const muon_config& cfg, int steps) {
+          const muon_config& cfg, int steps, bool noalloc) {
   g_scenario = std::string("full ") + name;
   unreg_all();
+  reg(scratch_buffer(), kNoallocScratchBytes, "no-alloc scratch");
   HostSet hs;
   const int32_t n = int32_t(shapes.size()) + n_adam;
   for (int32_t i = 0; i < n; ++i) {
@@ -596,7 +612,13 @@ void full(const char* name, const std::vector<std::pair<int64_t, int64_t>>& shap
     need(v.ptr, 4.0 * v.rows * v.cols, "muon_state view");
   }
   muon_free(ctx);
-  std::printf("full %-28s %4d tensors  %8.1f MB state\n", name, n, bytes / 1e6);
+  if (noalloc) {
+    const int32_t nm = int32_t(shapes.size());
+    for (int t = 0; t < steps; ++t)
+      if (muon_step_noalloc(&cfg, hs.p.data(), hs.g.data(), hs.m.data(), nm, t, nullptr) != MUON_OK)
+        fail("%s: muon_step_noalloc %d: %s", name, t, muon_last_error(nullptr));
+  }
+  std::printf("full %-28s %4d tensors  %8.1f MB state  noalloc %d\n", name, n, bytes / 1e6, int(noalloc));
 }
 
 }  // namespace chk
@@ -631,9 +653,20 @@ int main() {
   for (auto [nm, c] : {std::make_pair("ragged", def), std::make_pair("ragged fp32", f32),
                        std::make_pair("ragged two-pass", two), std::make_pair("ragged stored rows", rows),
                        std::make_pair("ragged 8 MiB cap", small_cap)}) {
-    full(nm, ragged, 3, c, 4);
+    full(nm, ragged, 3, c, 4, true);
   }
-  full("muonbp", {{512, 1024}, {1024, 512}, {384, 384}, {96, 4096}}, 1, bp, 4);
+  full("muonbp", {{512, 1024}, {1024, 512}, {384, 384}, {96, 4096}}, 1, bp, 4, true);
+  // the no-alloc entry point refuses a matrix whose workspace does not fit
+  {
+    g_scenario = "no-alloc refusal";
+    HostSet hs;
+    void* w = hs.add(4, "W");
+    muon_tensor p{w, 3072, 18432, 18432, MUON_F32, 0};
+    muon_tensor g{w, 3072, 18432, 18432, MUON_BF16, 0};
+    const long before = g_launches;
+    if (muon_step_noalloc(&def, &p, &g, &p, 1, 0, nullptr) != MUON_E_WORKSPACE || g_launches != before)
+      fail("no-alloc: a matrix beyond the scratch was not refused before any launch");
+  }
   std::printf("checks %ld  launches %ld  failures %ld\n", g_checks, g_launches, g_fail);
   return g_fail ? 1 : 0;
 }

@@ -8,8 +8,8 @@ and columns of W, G and M, partials, counters, Newton-Schulz workspaces and
 tiles) lies in a buffer the harness registered, and that tiles fit the padded
 shapes.  It runs the DiT-1.3B, DiT-4B, MuonBP and DiT-15B plans (host copies of
 the tables at a fake base address) in several configurations, and a ragged
-and a MuonBP set through muon_init, muon_step (with a pointer change)
-and the other entry points, with host memory behind them.
+and a MuonBP set through muon_init, muon_step (with a pointer change),
+muon_step_noalloc and the other entry points, with host memory behind them.
 """
 
 import os
