@@ -153,30 +153,72 @@ int row_chunk_class(int64_t cols) {
   return 0;
 }
 
-// Reorder a natural-order work list so the hardware's round-robin dispatch
-// (workgroup i -> XCD i mod 8) gives each XCD one contiguous segment of it:
-// neighbouring tiles, which share operand panels, then meet in the same L2.
+// Reorder a natural-order work list (each problem's tiles consecutive) for
+// the hardware's round-robin dispatch of workgroups to its 8 XCDs
+// (workgroup i -> XCD i mod 8), so that each XCD gets an equal share of the
+// work and neighbouring tiles, which share operand strips, meet in one XCD's
+// L2.
 //
-// With a cost per item, each XCD's segment is also ordered longest first
-// (stable, so a matrix's tiles stay together): the launch then ends on short
-// tiles instead of leaving most CUs idle behind a few long ones.
-template <typename T, typename Cost>
-void xcd_interleave(std::vector<T>& v, Cost cost) {
+// When every tile costs the same (the product and polynomial of same-sized
+// problems), each XCD takes one contiguous eighth of the list: its ~32
+// concurrent tiles then form whole super-blocks.  When costs differ (the
+// Gram's K is the long side, from d to 6d), equal counts per XCD would not
+// be equal work: each problem's tiles are cut into parts of up to kXcdPart
+// consecutive tiles (a small problem stays whole), and the parts, most
+// expensive tiles first, go to the least-loaded XCD that still has room
+// (split where one fills up).  Every XCD holds exactly n / 8 tiles, the
+// first n % 8 one more, so position p of the result goes to XCD p mod 8.
+// Each XCD's list is ordered longest tile first (stable): a launch then
+// ends on short tiles instead of leaving most CUs idle behind a few long
+// ones.
+constexpr int64_t kXcdPart = 8;    // tiles: fine enough to balance to about 1%
+
+template <typename T, typename Key, typename Cost>
+void xcd_interleave(std::vector<T>& v, Key key, Cost cost) {
   const int64_t n = static_cast<int64_t>(v.size());
   if (n < 16) return;
-  const int64_t q = n / 8, rem = n % 8;
-  for (int64_t x = 0; x < 8; ++x) {
-    const int64_t b = x * q + std::min<int64_t>(x, rem), e = b + q + (x < rem ? 1 : 0);
-    std::stable_sort(v.begin() + b, v.begin() + e,
-                     [&](const T& l, const T& r) { return cost(l) > cost(r); });
+  bool uniform = true;
+  for (const T& t : v) uniform = uniform && cost(t) == cost(v[0]);
+  std::vector<std::vector<T>> part(8);
+  if (uniform) {
+    const int64_t q = n / 8, rem = n % 8;
+    for (int64_t x = 0, o = 0; x < 8; ++x) {
+      const int64_t take = q + (x < rem ? 1 : 0);
+      part[x].assign(v.begin() + o, v.begin() + o + take);
+      o += take;
+    }
+  } else {
+    struct Part { int64_t b, e; double c; };
+    std::vector<Part> parts;
+    for (int64_t b = 0; b < n;) {
+      int64_t e = b + 1;
+      while (e < n && key(v[e]) == key(v[b])) ++e;
+      for (int64_t o = b; o < e; o += kXcdPart)
+        parts.push_back(Part{o, std::min(e, o + kXcdPart), double(cost(v[o]))});
+      b = e;
+    }
+    std::stable_sort(parts.begin(), parts.end(), [](const Part& l, const Part& r) { return l.c > r.c; });
+    const int64_t q = n / 8, rem = n % 8;
+    double load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (const Part& pt : parts)
+      for (int64_t o = pt.b; o < pt.e;) {
+        int best = -1;
+        for (int x = 0; x < 8; ++x)
+          if (int64_t(part[x].size()) < q + (x < rem ? 1 : 0) && (best < 0 || load[x] < load[best]))
+            best = x;
+        const int64_t take = std::min(pt.e - o, q + (best < rem ? 1 : 0) - int64_t(part[best].size()));
+        part[best].insert(part[best].end(), v.begin() + o, v.begin() + o + take);
+        load[best] += double(take) * pt.c;
+        o += take;
+      }
+    for (auto& pl : part)
+      std::stable_sort(pl.begin(), pl.end(), [&](const T& l, const T& r) { return cost(l) > cost(r); });
   }
   std::vector<T> out;
   out.reserve(v.size());
-  for (int64_t local = 0; local <= q; ++local)
-    for (int64_t x = 0; x < 8; ++x) {
-      const int64_t size = q + (x < rem ? 1 : 0);
-      if (local < size) out.push_back(v[x * q + std::min<int64_t>(x, rem) + local]);
-    }
+  for (size_t local = 0; local < part[0].size(); ++local)
+    for (int64_t x = 0; x < 8; ++x)
+      if (local < part[x].size()) out.push_back(part[x][local]);
   v.swap(out);
 }
 
@@ -274,12 +316,13 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
       }
     }
     // A tile costs its K: cp for the Gram, rp for the polynomial and product.
+    const auto prob = [](const GemmItem& g) { return g.ns; };
     for (int op = 0; op < 3; ++op)
       for (auto& gl : ch.gemm[op])
-        xcd_interleave(gl.items, [&](const GemmItem& g) {
+        xcd_interleave(gl.items, prob, [&](const GemmItem& g) {
           return op == kGemmGram ? ch.ns[g.ns].cp : ch.ns[g.ns].rp;
         });
-    xcd_interleave(ch.prod_wide.items, [&](const GemmItem& g) { return ch.ns[g.ns].rp; });
+    xcd_interleave(ch.prod_wide.items, prob, [&](const GemmItem& g) { return ch.ns[g.ns].rp; });
   }
   return chunks;
 }

@@ -426,6 +426,17 @@ void check_plan(const Plan& pl, const muon_config& cfg, const muon_tensor* param
   // NS coverage per chunk
   for (const auto* plan : {&pl.ns_full, &pl.ns_block})
     for (const NsChunk& ch : *plan) {
+      // workgroup p runs on XCD p mod 8: the K summed per XCD is balanced
+      for (int op = 0; op < 3; ++op)
+        for (const auto& gl : ch.gemm[op]) {
+          if (gl.items.size() < 1024) continue;
+          double c[8] = {0};
+          for (size_t q = 0; q < gl.items.size(); ++q)
+            c[q % 8] += double(op == kGemmGram ? ch.ns[gl.items[q].ns].cp : ch.ns[gl.items[q].ns].rp);
+          const double lo = *std::min_element(c, c + 8), hi = *std::max_element(c, c + 8);
+          ++g_checks;
+          if (hi > 1.03 * lo) fail("gemm op %d: XCD cost imbalance %.3f", op, hi / lo);
+        }
       const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
       for (int32_t k = 0; k < int32_t(ch.ns.size()); ++k) {
         const NsDev& d = ch.ns[k];
