@@ -12,6 +12,7 @@
 #include "../../matrix_aware_optimizer_periodic_amd/csrc/runtime.cpp"
 
 #include <cstdlib>
+#include <map>
 
 namespace chk {
 
@@ -89,11 +90,27 @@ void check_rows(const muon::MatDev* mats, const int32_t* ids, const int64_t* pre
   }
 }
 
+int64_t g_tall_limit = 0;   // the planner's residency bound for the single pass
+
 void check_tall(const muon::MatDev* mats, const muon::TileItem* tiles, int64_t ntiles,
                 const muon::TallSync* sync, const muon::TallCtl* ctl, const uint32_t* repair) {
   need(tiles, 8.0 * ntiles, "tall: tiles");
   need(ctl, sizeof(muon::TallCtl), "tall: control");
   need(repair, 4.0 * ntiles, "tall: repair list");
+  // Every wait ends if each strip's tiles lie within a window of at most
+  // g_tall_limit consecutive workgroups (a workgroup still waiting then holds
+  // one of at most window / 8 slots of its XCD), in chunk order; the planner
+  // lists each strip as one run of consecutive workgroups.
+  std::map<std::pair<int32_t, int32_t>, std::pair<int64_t, int32_t>> first_next;
+  for (int64_t b = 0; b < ntiles; ++b) {
+    const muon::TileItem it = tiles[b];
+    auto& fn = first_next[{it.id, it.tj}];
+    if (it.ti == 0) fn.first = b;
+    if (it.ti != fn.second) fail("tall: strip (%d, %d) chunk %d out of order", it.id, it.tj, it.ti);
+    fn.second = it.ti + 1;
+    if (b - fn.first + 1 > g_tall_limit)
+      fail("tall: strip (%d, %d) spans more than %lld workgroups", it.id, it.tj, (long long)g_tall_limit);
+  }
   for (int64_t b = 0; b < ntiles; ++b) {
     const muon::TileItem it = tiles[b];
     need(&mats[it.id], sizeof(muon::MatDev), "tall: mat entry");
@@ -103,11 +120,6 @@ void check_tall(const muon::MatDev* mats, const muon::TileItem* tiles, int64_t n
       fail("tall: matrix %d (%lld x %lld) cannot take the single pass", it.id, (long long)d.rows,
            (long long)d.cols);
     if (it.ti < 0 || it.ti >= nchunk || it.tj < 0 || it.tj >= nstrip) fail("tall: tile index");
-    // a strip's row chunks are consecutive workgroups, in order
-    const bool first = it.ti == 0;
-    if (!first && (b == 0 || tiles[b - 1].id != it.id || tiles[b - 1].tj != it.tj ||
-                   tiles[b - 1].ti != it.ti - 1))
-      fail("tall: tile %lld breaks its strip's run", (long long)b);
     mat_tensors(d, "tall: tensors");
     need(d.part, 4.0 * nstrip * (nchunk + 1) * muon::kTallCols, "tall: partial rows");
     need(&sync[d.sync0 + it.tj], sizeof(muon::TallSync), "tall: strip counters");
@@ -636,6 +648,7 @@ void full(const char* name, const std::vector<std::pair<int64_t, int64_t>>& shap
 
 int main() {
   using namespace chk;
+  g_tall_limit = fake_tall_limit();
   muon_config def;
   muon_config_default(&def);
   muon_config f32 = def, two = def, rows = def, bp = def, cap = def;
