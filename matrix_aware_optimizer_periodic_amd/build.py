@@ -16,8 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmuon_hip.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["kernels_rownorm.hip", "kernels_ns5.hip", "kernels_misc.hip", "noalloc.hip",
-           "runtime.cpp"]
+SOURCES = ["kernels_rownorm.hip", "kernels_ns5.hip", "kernels_gram_tri.hip", "kernels_misc.hip",
+           "noalloc.hip", "runtime.cpp"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -15,6 +15,7 @@
 // ns_workspace_max, and each chunk runs all its matrices through every
 // Newton-Schulz round with one grouped launch per product.
 #include "../../include/muon.h"
+#include "gram_tri.h"
 #include "muon_internal.h"
 
 #include <algorithm>
@@ -54,6 +55,8 @@ struct NsChunk {
   GemmList gemm[3][2];            // [op][tile == 256]
   GemmList prod_wide;             // bf16, 128-tile problems: 128 x 256 product tiles
                                   // for the rounds before the last
+  GemmList gram_tri;              // bf16 problems with rp == kTriRows: their whole
+                                  // Gram in one workgroup (ti, tj unused), largest cp first
   size_t off_ns = 0, off_prep = 0;
   size_t ws_bytes = 0;
 };
@@ -258,13 +261,29 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
   const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
   std::vector<NsChunk> chunks;
   NsChunk cur;
+  // Chunks are filled up to the cap, unless that leaves a last chunk under
+  // half the cap: its launches would hold a few CUs for about as long as a
+  // full chunk's (the r = 384 Gram runs one workgroup per problem).  Then
+  // every chunk is cut near total / count instead.
+  const uint64_t cap = cfg.ns_workspace_max;
+  size_t total = 0, fill = 0;
+  for (const Problem& p : probs) {
+    int64_t rp, cp;
+    int32_t np;
+    const size_t wb = problem_ws_bytes(p, tile_for(std::min(p.rows, p.cols)), es, &rp, &cp, &np);
+    total += wb;
+    fill = fill && cap && fill + wb > cap ? wb : fill + wb;
+  }
+  const bool balance = cap && total > cap && fill < cap / 2;
+  const size_t target = balance ? total / size_t((total + cap - 1) / cap) : SIZE_MAX;
   for (const Problem& p : probs) {
     int64_t rp, cp;
     int32_t nparts;
     const int64_t r = std::min(p.rows, p.cols);
     const int tile = tile_for(r);
     const size_t wb = problem_ws_bytes(p, tile, es, &rp, &cp, &nparts);
-    if (!cur.ns.empty() && cfg.ns_workspace_max && cur.ws_bytes + wb > cfg.ns_workspace_max) {
+    if (!cur.ns.empty() && cap &&
+        (cur.ws_bytes + wb > cap || (balance && cur.ws_bytes + wb / 2 > target))) {
       chunks.push_back(std::move(cur));
       cur = NsChunk();
     }
@@ -293,9 +312,11 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
         for (int64_t b = 0; b < sq / kPrepTile; ++b)
           ch.prep_items.push_back(TileItem{k, int16_t(a), int16_t(b)});
       const int64_t nr = d.rp / tile, nc = d.cp / tile;
+      const bool tri = es == 2 && d.rp == kTriRows;
+      if (tri) ch.gram_tri.items.push_back(GemmItem{k, 0, 0});
       for (int64_t i = 0; i < nr; ++i)
         for (int64_t j = i; j < nr; ++j) {
-          ch.gemm[kGemmGram][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+          if (!tri) ch.gemm[kGemmGram][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
           ch.gemm[kGemmPoly][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
         }
       // Product tiles in super-blocks of kSuperRows x kSuperCols tiles: the
@@ -323,6 +344,10 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
           return op == kGemmGram ? ch.ns[g.ns].cp : ch.ns[g.ns].rp;
         });
     xcd_interleave(ch.prod_wide.items, prob, [&](const GemmItem& g) { return ch.ns[g.ns].rp; });
+    // One workgroup per problem, each as long as its cp: longest first, so
+    // that the ones handed out last are short.
+    std::stable_sort(ch.gram_tri.items.begin(), ch.gram_tri.items.end(),
+                     [&](const GemmItem& x, const GemmItem& y) { return ch.ns[x.ns].cp > ch.ns[y.ns].cp; });
   }
   return chunks;
 }
@@ -485,6 +510,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
       for (auto& op : ch.gemm)
         for (auto& gl : op) gl.off = bump.take(gl.items.size() * sizeof(GemmItem));
       ch.prod_wide.off = bump.take(ch.prod_wide.items.size() * sizeof(GemmItem));
+      ch.gram_tri.off = bump.take(ch.gram_tri.items.size() * sizeof(GemmItem));
       ws = std::max(ws, ch.ws_bytes);
     }
   // 6. NS workspace, shared by all chunks of both plans
@@ -626,6 +652,7 @@ hipError_t upload_plan(hipStream_t s, char* base, const Plan& pl, const char** w
       for (const auto& op : ch.gemm)
         for (const auto& gl : op) up(gl.off, gl.items);
       up(ch.prod_wide.off, ch.prod_wide.items);
+      up(ch.gram_tri.off, ch.gram_tri.items);
     }
   return e;
 }
@@ -678,7 +705,13 @@ muon_status run_ns(muon_ctx* ctx, std::vector<NsChunk>& chunks) {
                              launch_ns_scale(ctx->stream, ns, int32_t(ch.ns.size()), c.ns_eps)));
     for (int it = 0; it < c.ns_iters; ++it) {
       const int last = it == c.ns_iters - 1;
-      for (int op = 0; op < 3; ++op)
+      for (int op = 0; op < 3; ++op) {
+        if (op == kGemmGram && !ch.gram_tri.items.empty()) {
+          const GemmItem* items = reinterpret_cast<const GemmItem*>(ctx->base + ch.gram_tri.off);
+          MUON_HIP(ctx, MUON_TIMED(ctx, MUON_K_NS_GRAM,
+                                   launch_ns_gram_tri(ctx->stream, ns, items,
+                                                      int64_t(ch.gram_tri.items.size()), it)));
+        }
         for (int t = 0; t < 2; ++t) {
           // before the last round, bf16 128-tile products run on 128 x 256 tiles
           const bool wide = op == kGemmProduct && t == 0 && !last && !ch.prod_wide.items.empty();
@@ -691,6 +724,7 @@ muon_status run_ns(muon_ctx* ctx, std::vector<NsChunk>& chunks) {
                                                   wide ? 256 : (t ? 256 : 128), prec, it, last, c.ns_a, c.ns_b, c.ns_c,
                                                   c.muon_wd)));
         }
+      }
     }
   }
   return MUON_OK;

@@ -205,6 +205,24 @@ void check_gemm(const muon::MatDev* mats, const muon::NsDev* ns, const muon::Gem
   }
 }
 
+// Whole-triangle Gram: one workgroup per listed bf16 problem with rp ==
+// kTriRows, reading X (rp x cp, whole 32-column k-steps) and writing A and
+// adiag; listed longest first.
+void check_gram_tri(const muon::NsDev* ns, const muon::GemmItem* items, int64_t nitems) {
+  need(items, 8.0 * nitems, "gram_tri: items");
+  int64_t prev = INT64_MAX;
+  for (int64_t b = 0; b < nitems; ++b) {
+    const muon::GemmItem it = items[b];
+    need(&ns[it.ns], sizeof(muon::NsDev), "gram_tri: ns entry");
+    const muon::NsDev& d = ns[it.ns];
+    check_ns_dev(d, 0, "gram_tri: workspace");
+    if (d.rp != muon::kTriRows) fail("gram_tri: problem %d has rp %lld", it.ns, (long long)d.rp);
+    if (d.cp < 256 || d.cp % 256) fail("gram_tri: cp %lld", (long long)d.cp);
+    if (d.cp > prev) fail("gram_tri: not listed longest first");
+    prev = d.cp;
+  }
+}
+
 void check_adam(const muon::AdamDev* t, const muon::AdamChunk* chunks, int64_t n) {
   need(chunks, 16.0 * n, "adamw: chunks");
   for (int64_t b = 0; b < n; ++b) {
@@ -266,6 +284,12 @@ hipError_t launch_fill_zero(hipStream_t, void* p, size_t bytes) {
   if (bytes % 4) chk::fail("fill_zero: %zu bytes", bytes);
   chk::need(p, double(bytes), "fill_zero");
   if (!chk::g_fail) std::memset(p, 0, bytes);
+  return hipSuccess;
+}
+hipError_t launch_ns_gram_tri(hipStream_t, const NsDev* ns, const GemmItem* items, int64_t nitems,
+                              int) {
+  ++chk::g_launches;
+  chk::check_gram_tri(ns, items, nitems);
   return hipSuccess;
 }
 hipError_t launch_rownorm_rows(hipStream_t, const MatDev* mats, const int32_t* ids,
@@ -395,6 +419,7 @@ void check_plan(const Plan& pl, const muon_config& cfg, const muon_tensor* param
       for (const auto& op : ch.gemm)
         for (const auto& gl : op) add(gl.off, gl.items.size() * sizeof(GemmItem), "gemm items");
       add(ch.prod_wide.off, ch.prod_wide.items.size() * sizeof(GemmItem), "wide product items");
+      add(ch.gram_tri.off, ch.gram_tri.items.size() * sizeof(GemmItem), "whole-triangle gram items");
       if (ch.ws_bytes > pl.ws_bytes) fail("chunk workspace over the reserved workspace");
     }
   add(pl.ws_base, pl.ws_bytes, "workspace");
@@ -454,12 +479,15 @@ void check_plan(const Plan& pl, const muon_config& cfg, const muon_tensor* param
         const NsDev& d = ch.ns[k];
         const int tile = d.r >= 1024 ? 256 : 128;
         const int64_t nr = d.rp / tile, nc = d.cp / tile;
-        int64_t gram = 0, prod = 0, prep = 0, wide = 0;
+        int64_t gram = 0, prod = 0, prep = 0, wide = 0, tri = 0;
         for (const GemmItem& g : ch.gemm[kGemmGram][tile == 256].items) gram += g.ns == k;
+        for (const GemmItem& g : ch.gram_tri.items) tri += g.ns == k;
         for (const GemmItem& g : ch.gemm[kGemmProduct][tile == 256].items) prod += g.ns == k;
         for (const GemmItem& g : ch.prod_wide.items) wide += g.ns == k;
         for (const TileItem& t : ch.prep_items) prep += t.id == k;
-        if (gram != nr * (nr + 1) / 2) fail("gram tiles of problem %d: %lld", k, (long long)gram);
+        const bool whole = es == 2 && d.rp == kTriRows;
+        if (gram != (whole ? 0 : nr * (nr + 1) / 2) || tri != (whole ? 1 : 0))
+          fail("gram of problem %d: %lld tiles, %lld whole", k, (long long)gram, (long long)tri);
         if (prod != nr * nc) fail("product tiles of problem %d", k);
         if (es == 2 && tile == 128 && wide != nr * (d.cp / 256)) fail("wide product tiles");
         if (prep != (d.rp / 64) * (d.cp / 64)) fail("prep tiles of problem %d", k);
@@ -554,9 +582,26 @@ void plan_only(const char* name, const std::vector<std::pair<int64_t, int64_t>>&
         check_gemm(pl.mats.data(), ch.ns.data(), ch.prod_wide.items.data(),
                    int64_t(ch.prod_wide.items.size()), kGemmProduct, 128, 256, prec, 0);
       }
+      if (!ch.gram_tri.items.empty()) {
+        reg(ch.gram_tri.items.data(), ch.gram_tri.items.size() * sizeof(GemmItem), "host tri");
+        check_gram_tri(ch.ns.data(), ch.gram_tri.items.data(), int64_t(ch.gram_tri.items.size()));
+      }
     }
-  std::printf("plan %-28s %4d matrices  %6.1f GB  %zu NS chunks  %zu tall tiles\n", name, n,
-              bytes / 1e9, nchunks, pl.tall_tiles.size());
+  // no chunk of a plan is a small remainder
+  double ws_lo = 0, ws_hi = 0;
+  for (const auto* plan : {&pl.ns_full, &pl.ns_block}) {
+    if (plan->size() < 2) continue;
+    double lo = 1e300, hi = 0;
+    for (const NsChunk& ch : *plan) {
+      lo = std::min(lo, double(ch.ws_bytes));
+      hi = std::max(hi, double(ch.ws_bytes));
+    }
+    ++g_checks;
+    if (lo < 0.5 * hi) fail("NS chunks of %.2f to %.2f GB", lo / 1e9, hi / 1e9);
+    ws_lo = lo; ws_hi = hi;
+  }
+  std::printf("plan %-28s %4d matrices  %6.1f GB  %zu NS chunks (%.2f-%.2f GB)  %zu tall tiles\n",
+              name, n, bytes / 1e9, nchunks, ws_lo / 1e9, ws_hi / 1e9, pl.tall_tiles.size());
 }
 
 // Full: host memory behind everything, through the public entry points.

@@ -340,8 +340,19 @@ def test_muonbp_blocks():
     their own with half the step size otherwise."""
     run_direction_parity([(512, 1024), (1024, 512), (384, 384)], 6, bp_blocks=8, bp_period=3,
                          ns_precision=1)
-    run_direction_parity([(512, 1024), (1024, 512)], 3, bp_blocks=8, bp_period=3,
-                         ns_precision=0)
+    # bf16: also blocks with r = 384 (384 x 384 and, tall, 768 x 384), whose
+    # Gram runs in one workgroup per block
+    run_direction_parity([(512, 1024), (1024, 512), (384, 3072), (768, 3072)], 3, bp_blocks=8,
+                         bp_period=3, ns_precision=0)
+
+
+def test_whole_triangle_gram_shapes():
+    """bf16 problems whose short side pads to 384 (r from 257 to 384) take the
+    Gram that computes all of A = X X^T in one workgroup: wide, tall and
+    square, ragged r and c, c up to 18432 (576 k-steps), over two refreshes
+    and the RowNorm steps between them, against the oracle."""
+    shapes = [(384, 3072), (3072, 384), (384, 384), (257, 1000), (1000, 300), (384, 18432)]
+    run_direction_parity(shapes, 4, ns_precision=0)
 
 
 def test_long_rows_streaming_path():
