@@ -91,12 +91,15 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, as_profiled: bool):
     """HBM bytes per launch of `kernel` from its committed counter summary
     (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy), or
-    None when there is none or it was taken on other sources."""
+    None when there is none, it was taken on other sources, or this run's
+    launches differ from the profiled ones (`as_profiled` false: another NS5
+    precision or workspace cap than the defaults the summaries were taken
+    with)."""
     path = os.path.join(HERE, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
-    if not os.path.exists(path):
+    if not as_profiled or not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):
@@ -292,6 +295,8 @@ def main() -> int:
         over["tall_single_pass"] = 0
     if args.ws_gib is not None:
         over["ns_workspace_max"] = int(args.ws_gib * 2 ** 30)
+    # the committed counter summaries were taken with these defaults
+    as_profiled = args.ns_precision == "bf16" and args.ws_gib is None and not args.tall_two_pass
     cfg = mm.muon_config_default(**over)
 
     dev = torch.device("cuda", 0)
@@ -432,7 +437,8 @@ def main() -> int:
             r = kernels[dom]
             roofline = {"kernel": dom, "bound": r["bound"], "achieved": r["achieved"],
                         "peak": r["peak"], "unit": r["unit"], "frac": r["frac"],
-                        "traffic": measured_traffic(dom, wl.name), "avg_launch_ms": r["avg_ms"],
+                        "traffic": measured_traffic(dom, wl.name, as_profiled),
+                        "avg_launch_ms": r["avg_ms"],
                         "work_per_launch": r["work_per_launch"]}
             if "min_bytes_per_launch" in r:
                 roofline["min_bytes_per_launch"] = r["min_bytes_per_launch"]
