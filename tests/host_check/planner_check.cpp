@@ -724,7 +724,10 @@ int main() {
                        std::make_pair("ragged 8 MiB cap", small_cap)}) {
     full(nm, ragged, 3, c, 4, true);
   }
-  full("muonbp", {{512, 1024}, {1024, 512}, {384, 384}, {96, 4096}}, 1, bp, 4, true);
+  // (384 x 3072: blocks with r = 384, and 3072 x 384: r = 384 on the full steps; their Gram runs
+  // one workgroup per problem)
+  full("muonbp", {{512, 1024}, {1024, 512}, {384, 384}, {96, 4096}, {384, 3072}, {3072, 384}}, 1, bp,
+       4, true);
   // the no-alloc entry point refuses a matrix whose workspace does not fit
   {
     g_scenario = "no-alloc refusal";
