@@ -13,13 +13,15 @@
 //
 // and the last round writes W -= lr * X straight into the stored layout.
 //
-// Layout.  X lives in the workspace twice: Xr (r x c, row-major) and Xc
-// (c x r, row-major, i.e. X^T).  Every product is then of the form
-// C[i][j] = sum_k P[i][k] Q[j][k] with both operands contiguous along k:
-// Gram P = Q = Xr; poly P = Q = A (symmetric); product P = B, Q = Xc.  The
-// product epilogue writes the new X into both layouts (Xr in place, Xc
-// ping-pong).  A tall stored matrix (m > n) is X^T, so it is read and
-// written through the same two layouts: no separate transpose pass.
+// Layout.  Every product is of the form C[i][j] = sum_k P[i][k] Q[j][k]:
+// Gram P = Q = X; poly P = Q = A (symmetric); product P = B, Q = X^T.  bf16
+// keeps X once, row-major (r x c), in two buffers that alternate between
+// rounds; the product stages its Q operand as rows of X and reads it
+// transposed from LDS.  fp32 keeps X (r x c, updated in place) and X^T
+// (c x r, two alternating buffers) and stages both operands along k.  A tall
+// stored matrix (m > n) is X^T: the prep kernel forms X from it through an
+// LDS transpose, and the last product writes W through its transposed
+// mirror pass, so no separate transpose kernel runs.
 // All workspace dims are padded to the tile size with zeros; zero padding is
 // preserved exactly by the three products, so the GEMMs need no bounds
 // checks and ragged shapes cost only the padded tiles.
