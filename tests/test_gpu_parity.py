@@ -346,6 +346,18 @@ def test_muonbp_blocks():
                          bp_period=3, ns_precision=0)
 
 
+def test_workspace_cap_splits_the_refresh_into_chunks():
+    """A workspace cap of 4 MiB splits the refresh into several chunks, each
+    run through every Newton-Schulz round before the next starts; a problem
+    larger than the cap (1200 x 1030) runs alone.  Under MuonBP, a 2 MiB cap
+    splits the block steps too, with r = 384 blocks in them.  Every step
+    matches the oracle as without the cap."""
+    shapes = [(300, 700), (700, 300), (1200, 1030), (384, 3072), (260, 260), (512, 256)]
+    run_direction_parity(shapes, 4, ns_workspace_max=4 << 20)
+    run_direction_parity([(384, 3072), (768, 3072), (512, 1024)], 3, bp_blocks=8, bp_period=3,
+                         ns_precision=0, ns_workspace_max=2 << 20)
+
+
 def test_whole_triangle_gram_shapes():
     """bf16 problems whose short side pads to 384 (r from 257 to 384) take the
     Gram that computes all of A = X X^T in one workgroup: wide, tall and
