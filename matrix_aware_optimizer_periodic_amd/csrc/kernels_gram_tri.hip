@@ -7,11 +7,12 @@
 // Block-Periodic Orthogonalization", abstract) on DiT widths of 3072: X is
 // 384 x c with c from 3072 to 18432.  Tiled, the upper triangle of A is six
 // 128-tiles, and each stages 2 x 128 rows of X per k-step for 128 x 128
-// outputs: 64 flops per staged byte, where the global->LDS path of a CU
-// delivers about 20 bytes per clock, a third of what the matrix cores
-// consume.  Here the workgroup stages the 384 rows of X once per k-step and
-// computes all 78 blocks (32 x 32) of the upper triangle from them: 213
-// flops per staged byte.
+// outputs: 64 flops per staged byte, where under full load the global->LDS
+// path delivers 20 to 29 bytes per clock per CU for such rows (64 bytes of
+// each, half a cache line), a third of what the matrix cores consume.  Here
+// the workgroup stages the 384 rows of X once per k-step and computes all 78
+// blocks (32 x 32) of the upper triangle from them: 213 flops per staged
+// byte.
 //
 // Work split.  Eight waves, two per SIMD (a wave's accumulators must fit
 // the 256 AGPRs; at 320 the compiler spills inside the loop).  Fragment f is
