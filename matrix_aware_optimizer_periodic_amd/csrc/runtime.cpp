@@ -176,8 +176,12 @@ int row_chunk_class(int64_t cols) {
 // ones.
 constexpr int64_t kXcdPart = 8;    // tiles: fine enough to balance to about 1%
 
+// part_size: the parts a problem's tiles are cut into when costs differ.
+// Larger parts keep more of an XCD's concurrent tiles on shared operand
+// strips (a Gram super-block); if they leave the per-XCD costs more than 2%
+// apart, the parts are cut to kXcdPart tiles instead.
 template <typename T, typename Key, typename Cost>
-void xcd_interleave(std::vector<T>& v, Key key, Cost cost) {
+void xcd_interleave(std::vector<T>& v, Key key, Cost cost, int64_t part_size = kXcdPart) {
   const int64_t n = static_cast<int64_t>(v.size());
   if (n < 16) return;
   bool uniform = true;
@@ -191,29 +195,37 @@ void xcd_interleave(std::vector<T>& v, Key key, Cost cost) {
       o += take;
     }
   } else {
-    struct Part { int64_t b, e; double c; };
-    std::vector<Part> parts;
-    for (int64_t b = 0; b < n;) {
-      int64_t e = b + 1;
-      while (e < n && key(v[e]) == key(v[b])) ++e;
-      for (int64_t o = b; o < e; o += kXcdPart)
-        parts.push_back(Part{o, std::min(e, o + kXcdPart), double(cost(v[o]))});
-      b = e;
-    }
-    std::stable_sort(parts.begin(), parts.end(), [](const Part& l, const Part& r) { return l.c > r.c; });
-    const int64_t q = n / 8, rem = n % 8;
-    double load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (const Part& pt : parts)
-      for (int64_t o = pt.b; o < pt.e;) {
-        int best = -1;
-        for (int x = 0; x < 8; ++x)
-          if (int64_t(part[x].size()) < q + (x < rem ? 1 : 0) && (best < 0 || load[x] < load[best]))
-            best = x;
-        const int64_t take = std::min(pt.e - o, q + (best < rem ? 1 : 0) - int64_t(part[best].size()));
-        part[best].insert(part[best].end(), v.begin() + o, v.begin() + o + take);
-        load[best] += double(take) * pt.c;
-        o += take;
+    // Parts of up to `ps` consecutive tiles of one problem, most expensive
+    // first, each to the least-loaded XCD that still has room (split where
+    // one fills up); returns the largest per-XCD cost over the smallest.
+    auto assign = [&](int64_t ps) {
+      for (auto& pl : part) pl.clear();
+      struct Part { int64_t b, e; double c; };
+      std::vector<Part> parts;
+      for (int64_t b = 0; b < n;) {
+        int64_t e = b + 1;
+        while (e < n && key(v[e]) == key(v[b])) ++e;
+        for (int64_t o = b; o < e; o += ps)
+          parts.push_back(Part{o, std::min(e, o + ps), double(cost(v[o]))});
+        b = e;
       }
+      std::stable_sort(parts.begin(), parts.end(), [](const Part& l, const Part& r) { return l.c > r.c; });
+      const int64_t q = n / 8, rem = n % 8;
+      double load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (const Part& pt : parts)
+        for (int64_t o = pt.b; o < pt.e;) {
+          int best = -1;
+          for (int x = 0; x < 8; ++x)
+            if (int64_t(part[x].size()) < q + (x < rem ? 1 : 0) && (best < 0 || load[x] < load[best]))
+              best = x;
+          const int64_t take = std::min(pt.e - o, q + (best < rem ? 1 : 0) - int64_t(part[best].size()));
+          part[best].insert(part[best].end(), v.begin() + o, v.begin() + o + take);
+          load[best] += double(take) * pt.c;
+          o += take;
+        }
+      return *std::max_element(load, load + 8) / *std::min_element(load, load + 8);
+    };
+    if (assign(part_size) > 1.02 && part_size > kXcdPart) assign(kXcdPart);
     for (auto& pl : part)
       std::stable_sort(pl.begin(), pl.end(), [&](const T& l, const T& r) { return cost(l) > cost(r); });
   }
@@ -315,10 +327,17 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
       const bool tri = es == 2 && d.rp == kTriRows;
       if (tri) ch.gram_tri.items.push_back(GemmItem{k, 0, 0});
       for (int64_t i = 0; i < nr; ++i)
-        for (int64_t j = i; j < nr; ++j) {
-          if (!tri) ch.gemm[kGemmGram][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+        for (int64_t j = i; j < nr; ++j)
           ch.gemm[kGemmPoly][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
-        }
+      // Gram: upper tiles in 4 x 4 super-blocks, each one XCD part below
+      // (its up to 16 tiles read 8 strips of X where single rows of tiles
+      // would read 17), so an XCD's concurrent tiles share strips in its L2.
+      if (!tri)
+        for (int64_t jb = 0; jb < nr; jb += 4)
+          for (int64_t ib = 0; ib < std::min(nr, jb + 4); ib += 4)
+            for (int64_t i = ib; i < std::min(nr, ib + 4); ++i)
+              for (int64_t j = std::max(jb, i); j < std::min(nr, jb + 4); ++j)
+                ch.gemm[kGemmGram][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
       // Product tiles in super-blocks of kSuperRows x kSuperCols tiles: the
       // ~32 tiles one XCD runs at a time then share a few B and X panels in
       // its L2 instead of streaming one B panel against 32 X panels.
@@ -337,12 +356,13 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
       }
     }
     // A tile costs its K: cp for the Gram, rp for the polynomial and product.
+    // Gram parts are whole super-blocks when that keeps the XCDs balanced.
     const auto prob = [](const GemmItem& g) { return g.ns; };
     for (int op = 0; op < 3; ++op)
       for (auto& gl : ch.gemm[op])
         xcd_interleave(gl.items, prob, [&](const GemmItem& g) {
           return op == kGemmGram ? ch.ns[g.ns].cp : ch.ns[g.ns].rp;
-        });
+        }, op == kGemmGram ? 16 : kXcdPart);
     xcd_interleave(ch.prod_wide.items, prob, [&](const GemmItem& g) { return ch.ns[g.ns].rp; });
     // One workgroup per problem, each as long as its cp: longest first, so
     // that the ones handed out last are short.
