@@ -1,9 +1,11 @@
 """muon_step_noalloc (no context, scratch in a static device array) against
 muon_step (the context's state buffer) on the same inputs, through the C ABI.
 
-Four calls in a row alternate a larger and a smaller set of matrices and
-both branches (a refresh step and a RowNorm step each), so every call finds
-the array holding the previous call's different layout; the outputs must
+Calls in a row alternate a larger and a smaller set of matrices and both
+branches (a refresh step and a RowNorm step each, one refresh of matrices
+whose short side is 384, which the whole-triangle Gram kernel takes, and one
+MuonBP block step), so every call finds the array holding the previous
+call's different layout; the outputs must
 match muon_step's to the tolerances of the optimizer's parity bar (momentum
 and RowNorm 1e-5, bf16-MFMA NS5 2e-2, relative Frobenius of the update).
 The same kernels run on the same values, so they are expected to match bit
@@ -21,6 +23,7 @@ pytestmark = pytest.mark.gpu
 
 BIG = [(1000, 300), (512, 1536), (2200, 2048), (6144, 2048)]
 SMALL = [(256, 512), (700, 300)]
+TRI = [(384, 3072), (3072, 384), (384, 384)]    # short side 384: the whole-triangle Gram kernel
 
 
 def _lib():
@@ -80,7 +83,7 @@ def _call_pair(m, shapes, t, seed, **over):
 
 def test_noalloc_matches_muon_step_on_consecutive_calls():
     m = _lib()
-    calls = [(BIG, 0, {}), (SMALL, 1, {}), (BIG, 1, {}), (SMALL, 3, {}),
+    calls = [(BIG, 0, {}), (SMALL, 1, {}), (TRI, 3, {}), (BIG, 1, {}), (SMALL, 3, {}),
              ([(512, 1024), (1024, 512)], 2, dict(bp_blocks=8, bp_period=3))]
     same = [_call_pair(m, shapes, t, 20 + k, **over) for k, (shapes, t, over) in enumerate(calls)]
     print(f"bitwise equal per call: {same}", flush=True)
