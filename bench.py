@@ -49,18 +49,20 @@ def ns5_class_flops(shapes, iters=5):
             "ns_product_last": x}
 
 
-def ns5_class_bytes(shapes, es=2):
+def ns5_class_bytes(shapes, es=2, lo=False):
     """Minimal HBM bytes per launch-set of each NS5 product class: every
     operand read once and every result written once (es = workspace bytes
     per value).  Gram: read X, write A; poly: read A, write B; product: read
-    B and X, write X; last product: read B, X and W (fp32), write W."""
+    B and X, write X; last product: read B, X and W (fp32), write W.  With X's
+    bf16 remainder (lo) the product also reads and rewrites it, and the last
+    product reads it."""
     g = p = x = xl = 0.0
     for m, n in shapes:
         r, c = min(m, n), max(m, n)
         g += es * (r * c + r * r)
         p += es * 2 * r * r
-        x += es * (r * r + 2 * r * c)
-        xl += es * (r * r + r * c) + 8 * r * c
+        x += es * (r * r + 2 * r * c) + (4 * r * c if lo else 0)
+        xl += es * (r * r + r * c) + 8 * r * c + (2 * r * c if lo else 0)
     return {"ns_gram": g, "ns_poly": p, "ns_product": x, "ns_product_last": xl}
 
 
@@ -254,7 +256,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=12)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dit-15b", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--ns-precision", choices=["bf16", "f32"], default="bf16")
+    ap.add_argument("--ns-precision", choices=["bf16", "bf16-comp", "f32"], default="bf16",
+                    help="NS5 products: bf16 MFMA; bf16 with X's rounding remainder in the a X "
+                         "term; fp32 MFMA")
     ap.add_argument("--K", type=int, default=None, help="refresh period (default 3)")
     ap.add_argument("--no-adamw", action="store_true", help="leave out the bias vectors")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -290,7 +294,8 @@ def main() -> int:
     over = dict(wl.overrides)
     if args.K is not None:
         over["K"] = args.K
-    over["ns_precision"] = mm.MUON_NS_BF16 if args.ns_precision == "bf16" else mm.MUON_NS_F32
+    over["ns_precision"] = {"bf16": mm.MUON_NS_BF16, "bf16-comp": mm.MUON_NS_BF16_COMP,
+                            "f32": mm.MUON_NS_F32}[args.ns_precision]
     if args.tall_two_pass:
         over["tall_single_pass"] = 0
     if args.ws_gib is not None:
@@ -381,7 +386,7 @@ def main() -> int:
     n_refresh = branches.count(mm.MUON_BRANCH_NS5)
 
     # ---- NS5 and RowNorm figures -------------------------------------------
-    peak_mm = PEAK_BF16 if args.ns_precision == "bf16" else PEAK_F32
+    peak_mm = PEAK_F32 if args.ns_precision == "f32" else PEAK_BF16
     fl = ns5_class_flops(shapes, cfg.ns_iters)
     f_refresh = sum(fl.values())
     # MuonBP block steps orthogonalise bp_blocks column blocks of each matrix
@@ -412,7 +417,8 @@ def main() -> int:
     kernels = {}
     if kt:
         nb = rownorm_class_bytes(shapes, gbytes, bool(cfg.tall_single_pass))
-        nsb = ns5_class_bytes(shapes, 2 if args.ns_precision == "bf16" else 4)
+        nsb = ns5_class_bytes(shapes, 4 if args.ns_precision == "f32" else 2,
+                              lo=args.ns_precision == "bf16-comp")
         n_rn = branches.count(mm.MUON_BRANCH_ROWNORM)
         for name, (ms, cnt) in kt.items():
             if cnt == 0:
@@ -472,7 +478,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": args.ns_precision,
+        "dtype": "f32" if args.ns_precision == "f32" else "bf16",
         "data": "synthetic",
         "config": {
             "workload": wl.name, "d": wl.d, "blocks": wl.blocks, "matrices": len(shapes),

@@ -89,10 +89,20 @@ typedef enum muon_branch_id {
   MUON_BRANCH_BLOCK_NS5 = 2  /* MuonBP: NS5 of each column block on its own */
 } muon_branch_id;
 
-/* Arithmetic of the NS5 matrix products. */
+/* Arithmetic of the NS5 matrix products.  The pages fix no precision for
+ * the iteration X <- a X + (b A + c A A) X; these are this library's choices. */
 typedef enum muon_ns_precision {
-  MUON_NS_BF16 = 0,  /* bf16 MFMA operands, fp32 accumulation             */
-  MUON_NS_F32 = 1    /* fp32 MFMA operands and accumulation               */
+  MUON_NS_BF16 = 0,      /* bf16 MFMA operands, fp32 accumulation          */
+  MUON_NS_F32 = 1,       /* fp32 MFMA operands and accumulation            */
+  MUON_NS_BF16_COMP = 2  /* as MUON_NS_BF16, and the a X term of every round
+                          * also takes X's bf16 rounding remainder, kept as
+                          * a second bf16 array (2 more workspace bytes per
+                          * element, 4 more bytes moved per element and
+                          * round).  It keeps singular directions far below
+                          * the largest from being lost to X's rounding:
+                          * on spectra spread over decades the bf16 form
+                          * deviates from the exact iteration by 2-7e-2,
+                          * this one by under 1e-2.                       */
 } muon_ns_precision;
 
 /* A dense row-major device tensor.  rows, cols >= 1 and ld == cols.

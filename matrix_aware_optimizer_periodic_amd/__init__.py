@@ -11,7 +11,7 @@ from __future__ import annotations
 
 from .binding import (  # noqa: F401
     EXPORTED, KERNEL_CLASSES, MUON_BF16, MUON_BRANCH_BLOCK_NS5, MUON_BRANCH_NS5, MUON_BRANCH_ROWNORM, MUON_F32,
-    MUON_KIND_ADAMW, MUON_KIND_MATRIX, MUON_NS_BF16, MUON_NS_F32, MuonConfig, MuonError,
+    MUON_KIND_ADAMW, MUON_KIND_MATRIX, MUON_NS_BF16, MUON_NS_BF16_COMP, MUON_NS_F32, MuonConfig, MuonError,
     MuonTensor, lib, muon_branch, muon_config_default, muon_free, muon_init, muon_last_error,
     muon_state, muon_state_bytes, muon_status_str, muon_step, muon_step_noalloc, muon_sync,
     muon_tall_giveups,

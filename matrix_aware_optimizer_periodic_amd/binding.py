@@ -19,7 +19,7 @@ MUON_OK, MUON_E_ARG, MUON_E_SHAPE, MUON_E_DTYPE, MUON_E_ALIGN, MUON_E_WORKSPACE,
 MUON_F32, MUON_BF16 = 0, 1
 MUON_KIND_MATRIX, MUON_KIND_ADAMW = 0, 1
 MUON_BRANCH_ROWNORM, MUON_BRANCH_NS5, MUON_BRANCH_BLOCK_NS5 = 0, 1, 2
-MUON_NS_BF16, MUON_NS_F32 = 0, 1
+MUON_NS_BF16, MUON_NS_F32, MUON_NS_BF16_COMP = 0, 1, 2
 
 EXPORTED = ("muon_config_default", "muon_state_bytes", "muon_init", "muon_step", "muon_state",
             "muon_branch", "muon_free", "muon_status_str", "muon_last_error",

@@ -117,12 +117,23 @@ __device__ __forceinline__ void prep_rows_vec(const MatDev& mt, int64_t ld, int6
   }
 }
 
+// The bf16 rounding remainders v - bf16(v) of four values whose bf16 pairs
+// are packed in lo, hi, stored as bf16 (the second half of a two-term split
+// of v: X = hi + remainder to about 16 significant bits).
+__device__ __forceinline__ void store_rem4(uint16_t* o, const float v[4], uint32_t lo, uint32_t hi) {
+  const float r0 = v[0] - bf16_to_f32(lo & 0xffffu), r1 = v[1] - bf16_to_f32(lo >> 16);
+  const float r2 = v[2] - bf16_to_f32(hi & 0xffffu), r3 = v[3] - bf16_to_f32(hi >> 16);
+  *as_global(reinterpret_cast<u32x2_t*>(o)) = u32x2_t{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
+}
+
 // ---------------------------------------------------------------------------
 // Refresh-step preparation, one 64 x 64 tile of the padded stored block per
 // workgroup: M <- beta M + G for the tile's valid elements, the tile's sum of
 // squares (one partial per tile), and the new M, unscaled, cast to the
 // workspace type: X = M (wide) or M^T (tall, through an LDS transpose) into
-// x[0], and for fp32 also X^T into xt[0]; padding is written as 0.
+// x[0], and for fp32 also X^T into xt[0]; padding is written as 0.  Where
+// the problem has xlo (bf16 with the remainder), X's bf16 rounding remainder
+// X - bf16(X) goes there in the same layout.
 // The pre-normalisation factor s = 1 / (||M||_F + eps) is applied by the
 // first Newton-Schulz round instead (A = s^2 X X^T, X_1 = s (a X + B X)),
 // which saves a second pass over M.
@@ -187,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
       const uint32_t lo = pack_bf16x2(v[0], v[1]);
       const uint32_t hi = pack_bf16x2(v[2], v[3]);
       *as_global(reinterpret_cast<u32x2_t*>(o)) = u32x2_t{lo, hi};
+      if (d.xlo) store_rem4(static_cast<uint16_t*>(d.xlo) + p * ldd + q0 + tc, v, lo, hi);
     } else {
       *as_global(reinterpret_cast<f32x4_t*>(o)) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
@@ -205,6 +217,7 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
       const uint32_t lo = pack_bf16x2(v[0], v[1]);
       const uint32_t hi = pack_bf16x2(v[2], v[3]);
       *as_global(reinterpret_cast<u32x2_t*>(o)) = u32x2_t{lo, hi};
+      if (d.xlo) store_rem4(static_cast<uint16_t*>(d.xlo) + (q0 + lq) * ldt + p0 + tc, v, lo, hi);
     } else {
       *as_global(reinterpret_cast<f32x4_t*>(o)) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
@@ -403,7 +416,7 @@ __device__ __forceinline__ u32x4_t buffer_rsrc(const void* p, int64_t nbytes) {
   return u32x4_t{unsigned(a), unsigned(a >> 32) & 0xffffu, unsigned(nbytes), 0x00020000u};
 }
 
-template <typename T, int BM, int WGM, int WGN, int OP, int BN = BM>
+template <typename T, int BM, int WGM, int WGN, int OP, int BN = BM, bool XLO = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const MatDev* __restrict__ mats, const NsDev* __restrict__ ns,
     const GemmItem* __restrict__ items, int iter, float ca, float cb, float cc,
@@ -414,6 +427,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // bf16 product: the X operand is staged from row-major X (32 rows of k by
   // the tile's BM columns) and read with transposed LDS loads.
   constexpr bool QT = PROD && sizeof(T) == 2;
+  // XLO (bf16 products with X's remainder): the a X term also takes a xlo,
+  // and a round before the last stores its output's remainder back to xlo.
+  static_assert(!XLO || QT, "the remainder is a bf16 product option");
   constexpr int NW = WGM * WGN;
   constexpr int NT = 64 * NW;                // threads
   // Output tiles are BM x BN: square except for the bf16 product, which may
@@ -780,11 +796,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // in batches of MB chunks, double-buffered the same way, its first batch
   // issued before the direct pass.
   const bool aux_is_w = last && !d.tall;     // also the W values to update
-  const bool need_aux = OP == kGemmPoly || (PROD && (!QT || aux_is_w));
+  const bool need_aux = OP == kGemmPoly || (PROD && (!QT || XLO || aux_is_w));
   const bool mirror_w = last && d.tall;
   // Batch sizes: as many chunks in flight as registers allow without spills
   // (the two W paths share one double buffer of 4-chunk batches).
-  constexpr int PBMAX = sizeof(T) == 4 ? (last ? 1 : 2) : 4;
+  constexpr int PBMAX = sizeof(T) == 4 ? (last ? 1 : 2) : (XLO && last ? 1 : 4);
   constexpr int PB = DIT < PBMAX ? DIT : PBMAX;
   constexpr int NB = DIT / PB;
   static_assert(NB * PB == DIT, "whole batches");
@@ -811,6 +827,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         const int64_t i = ib0 + r, j = j0 + ch * 8;
         if constexpr (OP == kGemmPoly) ra[bt & 1][q].load(static_cast<const T*>(d.a) + i * d.rp + j);
         else if constexpr (!QT) ra[bt & 1][q].load(xin + i * d.cp + j);
+        else if constexpr (XLO) ra[bt & 1][q].load(static_cast<const T*>(d.xlo) + i * d.cp + j);
         if (aux_is_w) wb[bt & 1][q].load(w, i * d.ld + d.col0 + j, wide_nv(i, j));
       }
     };
@@ -921,16 +938,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           store8(static_cast<T*>(d.b) + i * d.rp + j, v);
           writeback = true;
         } else {
-          // fp32: add (a + B_ii) X_i here; bf16: the MFMAs already did
+          // fp32: add (a + B_ii) X_i here; bf16: the MFMAs already did, on
+          // bf16(X), and XLO adds a times X's remainder
           float mlt = 0.f, xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
           if constexpr (!QT) {
             mlt = ca + d.bdiag[i];
+            ra[bt & 1][q].unpack(xv);
+          } else if constexpr (XLO) {
+            mlt = ca;
             ra[bt & 1][q].unpack(xv);
           }
           if constexpr (!last) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
             store8(xout + i * d.cp + j, v);
+            if constexpr (XLO) {
+              float rem[8];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) rem[u] = v[u] - bf16_to_f32(f32_to_bf16(v[u]));
+              store8(static_cast<T*>(d.xlo) + i * d.cp + j, rem);
+            }
             writeback = !QT;                // fp32 also writes X^T from the stage
           } else if (!d.tall) {
 #pragma unroll
@@ -1000,16 +1027,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
 // holds its 128 x 128 accumulators in the 256 AGPRs.
 template <int BM, int OP> struct WaveGrid { static constexpr int M = 2, N = 2; };
 
-template <typename T, int BM, int OP, int BN = BM>
+template <typename T, int BM, int OP, int BN = BM, bool XLO = false>
 void launch_gemm_op(hipStream_t s, const MatDev* mats, const NsDev* ns, const GemmItem* items,
                     int64_t nitems, int iter, float a, float b, float c, float wd) {
   constexpr int GM = WaveGrid<BM, OP>::M, GN = WaveGrid<BM, OP>::N;
-  ns_gemm_kernel<T, BM, GM, GN, OP, BN>
+  ns_gemm_kernel<T, BM, GM, GN, OP, BN, XLO>
       <<<dim3(static_cast<unsigned>(nitems)), dim3(64 * GM * GN), 0, s>>>(mats, ns, items, iter, a,
                                                                           b, c, wd);
 }
 
-template <typename T, int BM>
+template <typename T, int BM, bool XLO = false>
 hipError_t launch_gemm_t(hipStream_t s, const MatDev* mats, const NsDev* ns,
                          const GemmItem* items, int64_t nitems, int op, int iter, int last,
                          float a, float b, float c, float wd) {
@@ -1022,9 +1049,9 @@ hipError_t launch_gemm_t(hipStream_t s, const MatDev* mats, const NsDev* ns,
       break;
     default:
       if (last)
-        launch_gemm_op<T, BM, kGemmProductLast>(s, mats, ns, items, nitems, iter, a, b, c, wd);
+        launch_gemm_op<T, BM, kGemmProductLast, BM, XLO>(s, mats, ns, items, nitems, iter, a, b, c, wd);
       else
-        launch_gemm_op<T, BM, kGemmProduct>(s, mats, ns, items, nitems, iter, a, b, c, wd);
+        launch_gemm_op<T, BM, kGemmProduct, BM, XLO>(s, mats, ns, items, nitems, iter, a, b, c, wd);
       break;
   }
   return hipGetLastError();
@@ -1036,7 +1063,7 @@ hipError_t launch_ns_prep(hipStream_t s, const MatDev* mats, const NsDev* ns,
                           const TileItem* items, int64_t nitems, int prec, float beta) {
   if (nitems <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(nitems)), block(kThreads);
-  if (prec == 0)
+  if (prec != 1)   // bf16, with or without the remainder (its pointer tells)
     ns_prep_kernel<uint16_t><<<grid, block, 0, s>>>(mats, ns, items, beta);
   else
     ns_prep_kernel<float><<<grid, block, 0, s>>>(mats, ns, items, beta);
@@ -1057,12 +1084,19 @@ hipError_t launch_ns_gemm(hipStream_t s, const MatDev* mats, const NsDev* ns,
     // the one wide tile: 128 x 256 for the bf16 product of the rounds
     // before the last (short K: twice the work per tile prologue/epilogue
     // and a third fewer staged bytes per flop than 128 x 128)
-    if (prec != 0 || tile != 128 || tile_n != 256 || op != kGemmProduct || last)
+    if (prec == 1 || tile != 128 || tile_n != 256 || op != kGemmProduct || last)
       return hipErrorInvalidValue;
-    launch_gemm_op<uint16_t, 128, kGemmProduct, 256>(s, mats, ns, items, nitems, iter, a, b, c, wd);
+    if (prec == 2)
+      launch_gemm_op<uint16_t, 128, kGemmProduct, 256, true>(s, mats, ns, items, nitems, iter, a, b, c, wd);
+    else
+      launch_gemm_op<uint16_t, 128, kGemmProduct, 256>(s, mats, ns, items, nitems, iter, a, b, c, wd);
     return hipGetLastError();
   }
-  if (prec == 0) {
+  if (prec == 2 && op == kGemmProduct) {   // the Gram and polynomial do not read X's remainder
+    if (tile == 256) return launch_gemm_t<uint16_t, 256, true>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
+    return launch_gemm_t<uint16_t, 128, true>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
+  }
+  if (prec != 1) {
     if (tile == 256) return launch_gemm_t<uint16_t, 256>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
     return launch_gemm_t<uint16_t, 128>(s, mats, ns, items, nitems, op, iter, last, a, b, c, wd);
   }

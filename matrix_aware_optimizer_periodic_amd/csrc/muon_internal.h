@@ -87,6 +87,8 @@ struct NsDev {
   float* adiag;      // rp: diagonal of A kept in fp32
   float* bdiag;      // rp, fp32: B_ii (stored B has 0 there); bf16: stored B
                      // holds bf16(a + B_ii) and this the rounding remainder
+  void* xlo;         // MUON_NS_BF16_COMP: bf16(X - bf16(X)), rp x cp like
+                     // x[0], updated in place by each round's product; else null
   int32_t nparts;
   float lr;          // learning rate applied by the final product
 };
@@ -145,7 +147,9 @@ hipError_t launch_rownorm_repair(hipStream_t s, const MatDev* mats, const TileIt
                                  StepScalars sc);
 // Workgroups of the single-pass tall kernel that fit on one CU at once.
 hipError_t rownorm_tall_resident(int* workgroups_per_cu);
-// Refresh prep: momentum, Frobenius partials, unscaled X0 in both layouts.
+// Refresh prep: momentum, Frobenius partials, unscaled X0 in both layouts
+// (and its bf16 remainder where the problem has xlo).  prec: 0 bf16, 1 fp32,
+// 2 bf16 with the remainder (muon_ns_precision).
 hipError_t launch_ns_prep(hipStream_t s, const MatDev* mats, const NsDev* ns,
                           const TileItem* items, int64_t nitems, int prec, float beta);
 hipError_t launch_ns_scale(hipStream_t s, NsDev* ns_dev, int32_t count, float eps);

@@ -105,8 +105,9 @@ muon_status check_config(const muon_config* c, std::string& err) {
   if (!(c->eps_row >= 0.f) || !(c->ns_eps >= 0.f) || !(c->adam_eps >= 0.f)) {
     err = "eps values must be >= 0"; return MUON_E_ARG;
   }
-  if (c->ns_precision != MUON_NS_BF16 && c->ns_precision != MUON_NS_F32) {
-    err = "ns_precision must be MUON_NS_BF16 or MUON_NS_F32"; return MUON_E_ARG;
+  if (c->ns_precision != MUON_NS_BF16 && c->ns_precision != MUON_NS_F32 &&
+      c->ns_precision != MUON_NS_BF16_COMP) {
+    err = "ns_precision must be MUON_NS_BF16, MUON_NS_F32 or MUON_NS_BF16_COMP"; return MUON_E_ARG;
   }
   if (c->rownorm_axis != 0 && c->rownorm_axis != 1) { err = "rownorm_axis must be 0 or 1"; return MUON_E_ARG; }
   if (c->tall_single_pass != 0 && c->tall_single_pass != 1) { err = "tall_single_pass must be 0 or 1"; return MUON_E_ARG; }
@@ -248,8 +249,8 @@ struct Problem {
 // products before the last round use 128 x 256 tiles.
 int col_tile(int tile, size_t es) { return tile == 128 && es == 2 ? 256 : tile; }
 
-size_t problem_ws_bytes(const Problem& p, int tile, size_t es, int64_t* rp_out, int64_t* cp_out,
-                        int32_t* nparts_out) {
+size_t problem_ws_bytes(const Problem& p, int tile, size_t es, bool xlo, int64_t* rp_out,
+                        int64_t* cp_out, int32_t* nparts_out) {
   const int64_t r = std::min(p.rows, p.cols), c = std::max(p.rows, p.cols);
   const int ct = col_tile(tile, es);
   const int64_t rp = ceil_div(r, tile) * tile, cp = ceil_div(c, ct) * ct;
@@ -257,6 +258,7 @@ size_t problem_ws_bytes(const Problem& p, int tile, size_t es, int64_t* rp_out, 
   *rp_out = rp; *cp_out = cp; *nparts_out = nparts;
   size_t b = 0;
   b += 2 * align_up(size_t(rp) * cp * es, kAlign);      // bf16: x[0], x[1]; fp32: x[0], xt[0]
+  if (xlo) b += align_up(size_t(rp) * cp * 2, kAlign);   // bf16 remainder of X
   if (es == 4) b += align_up(size_t(cp) * rp * es, kAlign);   // fp32: xt[1]
   b += 2 * align_up(size_t(rp) * rp * es, kAlign);      // a, b
   b += align_up(size_t(nparts) * 4, kAlign);            // partials
@@ -270,35 +272,41 @@ int tile_for(int64_t r) { return r >= 1024 ? 256 : 128; }
 constexpr int64_t kSuperRows = 8, kSuperCols = 4;
 
 std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_config& cfg) {
-  const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
+  const size_t es = cfg.ns_precision == MUON_NS_F32 ? 4 : 2;
+  const bool xlo = cfg.ns_precision == MUON_NS_BF16_COMP;
   std::vector<NsChunk> chunks;
   NsChunk cur;
   // Chunks are filled up to the cap, unless that leaves a last chunk under
   // half the cap: its launches would hold a few CUs for about as long as a
   // full chunk's (the r = 384 Gram runs one workgroup per problem).  Then
-  // every chunk is cut near total / count instead.
+  // chunk k ends near k * total / count, the fewest chunks the cap allows
+  // (boundaries on the running total, so that per-chunk shortfalls do not
+  // add up to an extra chunk).
   const uint64_t cap = cfg.ns_workspace_max;
   size_t total = 0, fill = 0;
   for (const Problem& p : probs) {
     int64_t rp, cp;
     int32_t np;
-    const size_t wb = problem_ws_bytes(p, tile_for(std::min(p.rows, p.cols)), es, &rp, &cp, &np);
+    const size_t wb = problem_ws_bytes(p, tile_for(std::min(p.rows, p.cols)), es, xlo, &rp, &cp, &np);
     total += wb;
     fill = fill && cap && fill + wb > cap ? wb : fill + wb;
   }
   const bool balance = cap && total > cap && fill < cap / 2;
   const size_t target = balance ? total / size_t((total + cap - 1) / cap) : SIZE_MAX;
+  size_t pos = 0;   // bytes of the problems before this one
   for (const Problem& p : probs) {
     int64_t rp, cp;
     int32_t nparts;
     const int64_t r = std::min(p.rows, p.cols);
     const int tile = tile_for(r);
-    const size_t wb = problem_ws_bytes(p, tile, es, &rp, &cp, &nparts);
+    const size_t wb = problem_ws_bytes(p, tile, es, xlo, &rp, &cp, &nparts);
     if (!cur.ns.empty() && cap &&
-        (cur.ws_bytes + wb > cap || (balance && cur.ws_bytes + wb / 2 > target))) {
+        (cur.ws_bytes + wb > cap ||
+         (balance && pos + wb / 2 > (chunks.size() + 1) * target))) {
       chunks.push_back(std::move(cur));
       cur = NsChunk();
     }
+    pos += wb;
     NsDev d{};
     d.mat = p.mat;
     d.tall = p.rows > p.cols ? 1 : 0;
@@ -492,7 +500,7 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
   pl.ns_block = plan_ns(block, cfg);
   // The GEMM kernels address X (rp x cp) and A, B (rp x rp) through raw
   // buffer descriptors with 32-bit byte sizes and offsets.
-  const int64_t ns_es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
+  const int64_t ns_es = cfg.ns_precision == MUON_NS_F32 ? 4 : 2;
   for (auto* plan : {&pl.ns_full, &pl.ns_block})
     for (NsChunk& ch : *plan)
       for (const NsDev& d : ch.ns) {
@@ -552,7 +560,8 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
       a.v = static_cast<float*>(at(pl.v_off[i]));
     }
   }
-  const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
+  const size_t es = cfg.ns_precision == MUON_NS_F32 ? 4 : 2;
+  const bool xlo = cfg.ns_precision == MUON_NS_BF16_COMP;
   for (auto* plan : {&pl.ns_full, &pl.ns_block})
     for (NsChunk& ch : *plan)
       for (size_t k = 0; k < ch.ns.size(); ++k) {
@@ -563,11 +572,14 @@ muon_status build_plan(const muon_config& cfg, const muon_tensor* params, const 
           d.x[0] = at(o); o += xb;
           d.x[1] = at(o); o += xb;
           d.xt[0] = d.xt[1] = nullptr;
+          d.xlo = nullptr;
+          if (xlo) { d.xlo = at(o); o += xb; }
         } else {
           d.x[0] = at(o); o += xb;
           d.x[1] = nullptr;
           d.xt[0] = at(o); o += xb;
           d.xt[1] = at(o); o += xb;
+          d.xlo = nullptr;
         }
         d.a = at(o); o += align_up(size_t(d.rp) * d.rp * es, kAlign);
         d.b = at(o); o += align_up(size_t(d.rp) * d.rp * es, kAlign);
@@ -714,7 +726,7 @@ muon_status run_ns(muon_ctx* ctx, std::vector<NsChunk>& chunks) {
   const muon_config& c = ctx->cfg;
   const Plan& pl = ctx->plan;
   const MatDev* mats = reinterpret_cast<const MatDev*>(ctx->base + pl.off_mats);
-  const int prec = c.ns_precision == MUON_NS_BF16 ? 0 : 1;
+  const int prec = c.ns_precision;   // 0 bf16, 1 fp32, 2 bf16 with X's remainder
   for (NsChunk& ch : chunks) {
     NsDev* ns = reinterpret_cast<NsDev*>(ctx->base + ch.off_ns);
     const TileItem* prep = reinterpret_cast<const TileItem*>(ctx->base + ch.off_prep);

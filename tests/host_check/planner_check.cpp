@@ -140,9 +140,11 @@ void check_cols(const muon::MatDev* mats, const muon::TileItem* tiles, int64_t n
 }
 
 void check_ns_dev(const muon::NsDev& d, int prec, const char* k) {
-  const double es = prec ? 4 : 2;
+  const double es = prec == 1 ? 4 : 2;
   need(d.x[0], es * d.rp * d.cp, k);
-  if (prec) {
+  if (prec == 2) need(d.xlo, 2.0 * d.rp * d.cp, k);
+  else if (d.xlo) fail("%s: remainder buffer without the remainder precision", k);
+  if (prec == 1) {
     need(d.xt[0], es * d.rp * d.cp, k);
     need(d.xt[1], es * d.rp * d.cp, k);
   } else {
@@ -215,7 +217,7 @@ void check_gram_tri(const muon::NsDev* ns, const muon::GemmItem* items, int64_t 
     const muon::GemmItem it = items[b];
     need(&ns[it.ns], sizeof(muon::NsDev), "gram_tri: ns entry");
     const muon::NsDev& d = ns[it.ns];
-    check_ns_dev(d, 0, "gram_tri: workspace");
+    check_ns_dev(d, d.xlo ? 2 : 0, "gram_tri: workspace");   // reads X's bf16 part only
     if (d.rp != muon::kTriRows) fail("gram_tri: problem %d has rp %lld", it.ns, (long long)d.rp);
     if (d.cp < 256 || d.cp % 256) fail("gram_tri: cp %lld", (long long)d.cp);
     if (d.cp > prev) fail("gram_tri: not listed longest first");
@@ -347,7 +349,7 @@ hipError_t launch_ns_gemm(hipStream_t, const MatDev* mats, const NsDev* ns, cons
                           int64_t nitems, int op, int tile, int tile_n, int prec, int, int last,
                           float, float, float, float) {
   ++chk::g_launches;
-  if (tile_n != tile && (prec != 0 || tile != 128 || tile_n != 256 || op != kGemmProduct || last))
+  if (tile_n != tile && (prec == 1 || tile != 128 || tile_n != 256 || op != kGemmProduct || last))
     chk::fail("gemm: tile %d x %d not built for op %d prec %d last %d", tile, tile_n, op, prec, last);
   chk::check_gemm(mats, ns, items, nitems, op, tile, tile_n, prec, last);
   return hipSuccess;
@@ -474,7 +476,7 @@ void check_plan(const Plan& pl, const muon_config& cfg, const muon_tensor* param
           ++g_checks;
           if (hi > 1.03 * lo) fail("gemm op %d: XCD cost imbalance %.3f", op, hi / lo);
         }
-      const size_t es = cfg.ns_precision == MUON_NS_BF16 ? 2 : 4;
+      const size_t es = cfg.ns_precision == MUON_NS_F32 ? 4 : 2;
       for (int32_t k = 0; k < int32_t(ch.ns.size()); ++k) {
         const NsDev& d = ch.ns[k];
         const int tile = d.r >= 1024 ? 256 : 128;
@@ -561,7 +563,7 @@ void plan_only(const char* name, const std::vector<std::pair<int64_t, int64_t>>&
              reinterpret_cast<TallCtl*>(tb), reinterpret_cast<uint32_t*>(tb + sizeof(TallCtl)));
   reg(pl.col_tiles.data(), pl.col_tiles.size() * sizeof(TileItem), "host col tiles");
   check_cols(pl.mats.data(), pl.col_tiles.data(), int64_t(pl.col_tiles.size()));
-  const int prec = cfg.ns_precision == MUON_NS_BF16 ? 0 : 1;
+  const int prec = cfg.ns_precision;
   size_t nchunks = 0;
   for (const auto* plan : {&pl.ns_full, &pl.ns_block})
     for (const NsChunk& ch : *plan) {
@@ -696,8 +698,9 @@ int main() {
   g_tall_limit = fake_tall_limit();
   muon_config def;
   muon_config_default(&def);
-  muon_config f32 = def, two = def, rows = def, bp = def, cap = def;
+  muon_config f32 = def, two = def, rows = def, bp = def, cap = def, comp = def;
   f32.ns_precision = MUON_NS_F32;
+  comp.ns_precision = MUON_NS_BF16_COMP;
   two.tall_single_pass = 0;
   rows.rownorm_axis = 1;
   bp.bp_blocks = 8;
@@ -711,6 +714,7 @@ int main() {
   plan_only("dit-4b muonbp", dit(3072, 24), bp);
   plan_only("dit-15b", dit(5120, 32), def);
   plan_only("dit-15b 1 GiB workspace cap", dit(5120, 32), cap);
+  plan_only("dit-15b bf16 with X's remainder", dit(5120, 32), comp);
   plan_only("dit-15b muonbp", dit(5120, 32), bp);
   // ragged and edge shapes, through the entry points
   const std::vector<std::pair<int64_t, int64_t>> ragged = {
@@ -721,13 +725,17 @@ int main() {
   small_cap.ns_workspace_max = uint64_t(8) << 20;
   for (auto [nm, c] : {std::make_pair("ragged", def), std::make_pair("ragged fp32", f32),
                        std::make_pair("ragged two-pass", two), std::make_pair("ragged stored rows", rows),
-                       std::make_pair("ragged 8 MiB cap", small_cap)}) {
+                       std::make_pair("ragged 8 MiB cap", small_cap),
+                       std::make_pair("ragged bf16 with X's remainder", comp)}) {
     full(nm, ragged, 3, c, 4, true);
   }
   // (384 x 3072: blocks with r = 384, and 3072 x 384: r = 384 on the full steps; their Gram runs
   // one workgroup per problem)
   full("muonbp", {{512, 1024}, {1024, 512}, {384, 384}, {96, 4096}, {384, 3072}, {3072, 384}}, 1, bp,
        4, true);
+  muon_config bp_comp = bp;
+  bp_comp.ns_precision = MUON_NS_BF16_COMP;
+  full("muonbp bf16 with X's remainder", {{512, 1024}, {384, 3072}, {3072, 384}}, 1, bp_comp, 4, true);
   // the no-alloc entry point refuses a matrix whose workspace does not fit
   {
     g_scenario = "no-alloc refusal";

@@ -109,6 +109,10 @@ def test_state_bytes_counts_state_and_workspace():
     assert nbytes >= 4 * wl.elements + 4 * wl.elements   # momentum + two bf16 X buffers
     c32 = m.muon_config_default(ns_precision=m.MUON_NS_F32)
     assert m.muon_state_bytes(c32, ps, [0] * len(ps)) > nbytes
+    # bf16 with X's remainder: one more bf16 copy of every X (no cap: one chunk,
+    # and every DiT X is a whole number of 256-byte blocks)
+    comp = m.muon_config_default(ns_precision=m.MUON_NS_BF16_COMP)
+    assert m.muon_state_bytes(comp, ps, [0] * len(ps)) == nbytes + 2 * wl.elements
     adam = m.muon_state_bytes(c, [desc(1, 1000)], [m.MUON_KIND_ADAMW])
     assert 8000 <= adam < 8000 + 4096
     # a workspace cap splits the NS5 work and shrinks the buffer

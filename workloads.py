@@ -92,6 +92,34 @@ def host_weight0(seed: int, idx: int, shape, std: float = 0.02) -> np.ndarray:
     return host_normal(shape, std, "f32", seed, 2, idx)
 
 
+SPECTRA = ("geometric-1e-4", "geometric-1e-2", "rank-8th-noise", "one-spike")
+
+
+def host_spectrum_matrix(seed: int, idx: int, shape, kind: str, scale: float = 1e-2) -> np.ndarray:
+    """A float32 matrix U diag(s) V^T with random orthonormal U, V and a set
+    spectrum s over the short side r: falling geometrically from 1 to 1e-4 or
+    1e-2, r/8 ones plus N(0, 1e-6) noise everywhere, or one value 100 and the
+    rest 1.  Momenta of trained networks are far from the flat spectra of
+    i.i.d. gradients; these stand in for them."""
+    m, n = shape
+    r = min(m, n)
+    g = _rng(seed, 3, idx, SPECTRA.index(kind))
+    u, _ = np.linalg.qr(g.standard_normal((m, r)))
+    v, _ = np.linalg.qr(g.standard_normal((n, r)))
+    if kind == "geometric-1e-4":
+        s = 10.0 ** (-4.0 * np.arange(r) / r)
+    elif kind == "geometric-1e-2":
+        s = 10.0 ** (-2.0 * np.arange(r) / r)
+    elif kind == "rank-8th-noise":
+        s = np.r_[np.ones(max(1, r // 8)), np.zeros(r - max(1, r // 8))]
+    else:
+        s = np.r_[100.0, np.ones(r - 1)]
+    x = (u * s) @ v.T
+    if kind == "rank-8th-noise":
+        x = x + 1e-3 * g.standard_normal((m, n))
+    return (x * scale).astype(np.float32)
+
+
 # ------------------------------------------------------------------ device RNG
 def device_normal_(out, std: float, seed: int):
     """Fill a CUDA tensor in place with seeded N(0, std^2) values.
