@@ -26,7 +26,8 @@
 // w and w + 4 hold 19 or 20 together.
 //
 // Staging is the tiled kernel's: a ring of k-steps of 64 bytes per row
-// (32 bf16 values), filled by buffer_load ... lds issued ring - 1 steps ahead,
+// (32 bf16 values; X and A are k-block-major, so a k-step of all 384 rows is
+// one contiguous 24 KB run), filled by buffer_load ... lds issued ring - 1 steps ahead,
 // 16-byte chunk c of row r at position c ^ ((r >> 2) & 3), MFMA
 // v_mfma_f32_32x32x16_bf16 with the same operand layout.  Each wave
 // interleaves its MFMAs with its fragment reads and DMAs in fixed slots.
@@ -164,20 +165,21 @@ __device__ __forceinline__ void tri_wave(const NsDev& d, unsigned char* smem, in
 
   const int cur = iter & 1;
   const uint16_t* x = static_cast<const uint16_t*>(cur ? d.x[1] : d.x[0]);
-  const int64_t ldb = d.cp * 2;                 // bytes per row of X
   const int nk = int(d.cp / 32);                // k-steps
-  const u32x4_t rX = buffer_rsrc(x, int64_t(kTriRows) * ldb);
+  // X is k-block-major: k-step kc is rows 0 .. kTriRows - 1 of 64 bytes
+  // each, one contiguous run at kc * kStageBytes.
+  const u32x4_t rX = buffer_rsrc(x, int64_t(kTriRows) * d.cp * 2);
   // DMA block q of this wave: rows 16 (W + 8 q) .. + 15; lane l brings row
   // + (l >> 2), logical chunk (l & 3) ^ ((l >> 4) & 3), which lands at
   // physical chunk l & 3 (the row's swizzle).
   const unsigned offX =
-      unsigned((16 * W + (lane >> 2)) * ldb) + unsigned(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
-  const unsigned rstride = unsigned(16 * kWaves * ldb);
+      unsigned((16 * W + (lane >> 2)) * 64) + unsigned(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+  constexpr unsigned rstride = 16 * kWaves * 64;
   auto issue_one = [&](int kt, int q) {
     const int kc = min(kt, nk - 1);   // past the end: reload the last step
     LOCAL unsigned char* base =
         (LOCAL unsigned char*)(smem + (kt % kRing) * kStageBytes + (W + kWaves * q) * 1024);
-    dma16(rX, unsigned(uintptr_t(base)), offX + unsigned(q) * rstride, unsigned(kc * 64));
+    dma16(rX, unsigned(uintptr_t(base)), offX + unsigned(q) * rstride, unsigned(kc * kStageBytes));
   };
 
   f32x16_t acc[NB];
@@ -296,13 +298,14 @@ __device__ __forceinline__ void tri_wave(const NsDev& d, unsigned char* smem, in
       // block (bi, bj), row `row`: C[row][8 q + u] = S[8 q + u][row]
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = S[(8 * q + u) * kEpiPitch + row];
-      store8_bf16(A + (bi * 32 + row) * rp + bj * 32 + 8 * q, v);
+      // A is k-block-major too: (i, j) at ((j / 32) rp + i) 32 + j % 32
+      store8_bf16(A + (int64_t(bj) * rp + bi * 32 + row) * 32 + 8 * q, v);
       if (bi != bj) {
         // mirrored block (bj, bi), row `row`: C[8 q + u][row] = S[row][8 q + u]
         const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(S + row * kEpiPitch + 8 * q);
         const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(S + row * kEpiPitch + 8 * q + 4);
         const float m[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        store8_bf16(A + (bj * 32 + row) * rp + bi * 32 + 8 * q, m);
+        store8_bf16(A + (int64_t(bi) * rp + bj * 32 + row) * 32 + 8 * q, m);
       }
     }
     if (bi == bj && lane < 32) d.adiag[bi * 32 + lane] = S[lane * kEpiPitch + lane];

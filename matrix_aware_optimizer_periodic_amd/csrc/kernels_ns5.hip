@@ -15,9 +15,12 @@
 //
 // Layout.  Every product is of the form C[i][j] = sum_k P[i][k] Q[j][k]:
 // Gram P = Q = X; poly P = Q = A (symmetric); product P = B, Q = X^T.  bf16
-// keeps X once, row-major (r x c), in two buffers that alternate between
-// rounds; the product stages its Q operand as rows of X and reads it
-// transposed from LDS.  fp32 keeps X (r x c, updated in place) and X^T
+// keeps X once (r x c), in two buffers that alternate between rounds; the
+// product stages its Q operand as rows of X and reads it transposed from
+// LDS.  bf16 X, A and B are k-block-major (ws_at): per block of 32 columns,
+// all rows' 64 bytes one after another, so that every stage of every operand
+// is read as whole 128-byte lines (row-major rows of 64 bytes per stage would
+// be half lines, which cost the L2 as much as whole ones).  fp32 keeps X (r x c, updated in place) and X^T
 // (c x r, two alternating buffers) and stages both operands along k.  A tall
 // stored matrix (m > n) is X^T: the prep kernel forms X from it through an
 // LDS transpose, and the last product writes W through its transposed
@@ -117,6 +120,18 @@ __device__ __forceinline__ void prep_rows_vec(const MatDev& mt, int64_t ld, int6
   }
 }
 
+// Offset of element (i, j) of a workspace array with `rows` rows.  bf16
+// arrays (X, its remainder, A, B) are k-block-major: blocks of 32 columns,
+// each holding every row's 32 values (64 bytes) one after another, so that
+// one k-stage of any set of consecutive rows is a contiguous run of whole
+// 128-byte lines, and 8 consecutive values of a row stay contiguous.  fp32
+// arrays are row-major with leading dimension ld.
+template <typename T>
+__device__ __forceinline__ int64_t ws_at(int64_t i, int64_t j, int64_t rows, int64_t ld) {
+  if constexpr (sizeof(T) == 2) return ((j >> 5) * rows + i) * 32 + (j & 31);
+  return i * ld + j;
+}
+
 // The bf16 rounding remainders v - bf16(v) of four values whose bf16 pairs
 // are packed in lo, hi, stored as bf16 (the second half of a two-term split
 // of v: X = hi + remainder to about 16 significant bits).
@@ -193,12 +208,12 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
       tile[lr][tc + u] = v[u];
     }
     if (dst == nullptr) continue;
-    T* o = dst + p * ldd + q0 + tc;
+    T* o = dst + ws_at<T>(p, q0 + tc, d.rp, ldd);   // bf16: X itself (rp rows)
     if constexpr (sizeof(T) == 2) {
       const uint32_t lo = pack_bf16x2(v[0], v[1]);
       const uint32_t hi = pack_bf16x2(v[2], v[3]);
       *as_global(reinterpret_cast<u32x2_t*>(o)) = u32x2_t{lo, hi};
-      if (d.xlo) store_rem4(static_cast<uint16_t*>(d.xlo) + p * ldd + q0 + tc, v, lo, hi);
+      if (d.xlo) store_rem4(static_cast<uint16_t*>(d.xlo) + ws_at<T>(p, q0 + tc, d.rp, ldd), v, lo, hi);
     } else {
       *as_global(reinterpret_cast<f32x4_t*>(o)) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
@@ -212,12 +227,12 @@ __global__ __launch_bounds__(kThreads) void ns_prep_kernel(
     float v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = tile[tc + u][lq];
-    T* o = dstt + (q0 + lq) * ldt + p0 + tc;
+    T* o = dstt + ws_at<T>(q0 + lq, p0 + tc, d.rp, ldt);   // bf16: X itself (rp rows)
     if constexpr (sizeof(T) == 2) {
       const uint32_t lo = pack_bf16x2(v[0], v[1]);
       const uint32_t hi = pack_bf16x2(v[2], v[3]);
       *as_global(reinterpret_cast<u32x2_t*>(o)) = u32x2_t{lo, hi};
-      if (d.xlo) store_rem4(static_cast<uint16_t*>(d.xlo) + (q0 + lq) * ldt + p0 + tc, v, lo, hi);
+      if (d.xlo) store_rem4(static_cast<uint16_t*>(d.xlo) + ws_at<T>(q0 + lq, p0 + tc, d.rp, ldt), v, lo, hi);
     } else {
       *as_global(reinterpret_cast<f32x4_t*>(o)) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
@@ -341,7 +356,8 @@ template <> struct Raw8<float> {
 // product tiles of short-K problems.
 //
 // Operand staging.  The k loop runs over stages of 64 bytes of k (32 bf16 or
-// 16 fp32) for all BM + BN rows of P and Q, NSTAGE stages deep in LDS (4 for
+// 16 fp32; in bf16 one k-block of the operand's layout) for all BM + BN rows
+// of P and Q, NSTAGE stages deep in LDS (4 for
 // 256-tiles, 5 for 128-tiles, 3 for 128 x 256).  Global data goes straight to LDS (MUBUF
 // buffer_load ... lds: each lane's 16 bytes land at the wave's LDS base +
 // 16 * lane), issued NSTAGE - 1 stages ahead of its use, so no registers
@@ -514,14 +530,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   const int64_t qrow = QT ? d.rp : (PROD ? d.cp : d.rp);
   const u32x4_t rP = buffer_rsrc(P, prow * ld * int64_t(sizeof(T)));
   const u32x4_t rQ = buffer_rsrc(Q, qrow * ldq * int64_t(sizeof(T)));
-  const unsigned offP = unsigned((i0 + drow) * ld * int64_t(sizeof(T))) + unsigned(dchunk * 16);
-  const unsigned rstride = unsigned(int64_t(16 * NW) * ld * int64_t(sizeof(T)));
+  // bf16 operands are k-block-major (ws_at): a stage of P or Q rows is one
+  // contiguous run (64 B per row), and QT's 32 rows of X are, per 32
+  // columns, 2 KB contiguous.  fp32 operands are row-major.
+  constexpr bool BLK = sizeof(T) == 2;
+  const unsigned offP = BLK ? unsigned((i0 + drow) * 64 + dchunk * 16)
+                            : unsigned((i0 + drow) * ld * int64_t(sizeof(T))) + unsigned(dchunk * 16);
+  const unsigned rstride = BLK ? unsigned(16 * NW * 64) : unsigned(int64_t(16 * NW) * ld * int64_t(sizeof(T)));
   const unsigned offQ =
-      QT ? unsigned((int64_t(qtrow) * ldq + j0 + 8 * qtchunk) * int64_t(sizeof(T)))
-         : unsigned((j0 + drow) * ldq * int64_t(sizeof(T))) + unsigned(dchunk * 16);
-  const unsigned rstrideQ = unsigned(int64_t(QT ? RPB * NW : 16 * NW) * ldq * int64_t(sizeof(T)));
-  // bytes per stage along k: 64 (k contiguous) or KT rows of X (QT)
-  const int64_t kstepQ = QT ? int64_t(KT) * ldq * int64_t(sizeof(T)) : 64;
+      QT ? unsigned((j0 / 32 + qtchunk / 4) * qrow * 64 + qtrow * 64 + (qtchunk % 4) * 16)
+         : BLK ? unsigned((j0 + drow) * 64 + dchunk * 16)
+               : unsigned((j0 + drow) * ldq * int64_t(sizeof(T))) + unsigned(dchunk * 16);
+  const unsigned rstrideQ = BLK ? unsigned((QT ? RPB * NW : 16 * NW) * 64)
+                                : unsigned(int64_t(16 * NW) * ldq * int64_t(sizeof(T)));
+  // bytes per stage along k: P, one k-block of all prow rows (bf16) or 64;
+  // Q, likewise, or (QT) KT rows of one k-block
+  const int64_t kstepP = BLK ? prow * 64 : 64;
+  const int64_t kstepQ = QT ? int64_t(KT) * 64 : BLK ? qrow * 64 : 64;
   // Stages past the end are issued as a reload of the last stage: the loop
   // body then has no branches (exact wait counts), and the buffer such a
   // reload lands in is one no wave reads any more.
@@ -536,7 +561,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const int kc = min(kt, nk - 1);
     LOCAL unsigned char* base =
         (LOCAL unsigned char*)(smem + (kt % NSTAGE) * STAGE + swid * 1024);
-    const int kb = q < DMAP ? kc * 64 : int(kc * kstepQ);
+    const unsigned kb = q < DMAP ? unsigned(kc * kstepP) : unsigned(kc * kstepQ);
     const unsigned voff = q < DMAP ? offP + unsigned(q) * rstride
                                    : offQ + unsigned(q - DMAP) * rstrideQ;
     dma16(q < DMAP ? rP : rQ, unsigned(uintptr_t(base + q * NW * 1024)), voff, unsigned(kb));
@@ -825,9 +850,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         const int idx = tid + (bt * PB + q) * NT;
         const int r = idx / CPR, ch = idx % CPR;
         const int64_t i = ib0 + r, j = j0 + ch * 8;
-        if constexpr (OP == kGemmPoly) ra[bt & 1][q].load(static_cast<const T*>(d.a) + i * d.rp + j);
-        else if constexpr (!QT) ra[bt & 1][q].load(xin + i * d.cp + j);
-        else if constexpr (XLO) ra[bt & 1][q].load(static_cast<const T*>(d.xlo) + i * d.cp + j);
+        if constexpr (OP == kGemmPoly) ra[bt & 1][q].load(static_cast<const T*>(d.a) + ws_at<T>(i, j, d.rp, d.rp));
+        else if constexpr (!QT) ra[bt & 1][q].load(xin + ws_at<T>(i, j, d.rp, d.cp));
+        else if constexpr (XLO) ra[bt & 1][q].load(static_cast<const T*>(d.xlo) + ws_at<T>(i, j, d.rp, d.cp));
         if (aux_is_w) wb[bt & 1][q].load(w, i * d.ld + d.col0 + j, wide_nv(i, j));
       }
     };
@@ -907,7 +932,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
             for (int u = 0; u < 8; ++u) dv = (u == du) ? v[u] : dv;
             d.adiag[i] = dv;
           }
-          store8(static_cast<T*>(d.a) + i * d.rp + j, v);
+          store8(static_cast<T*>(d.a) + ws_at<T>(i, j, d.rp, d.rp), v);
         } else if constexpr (OP == kGemmPoly) {
           float av[8];
           ra[bt & 1][q].unpack(av);
@@ -935,7 +960,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
 #pragma unroll
           for (int u = 0; u < 8; ++u)
             v[u] = (has_diag && u == du) ? dval : fmaf(cc, v[u], cb * av[u]);
-          store8(static_cast<T*>(d.b) + i * d.rp + j, v);
+          store8(static_cast<T*>(d.b) + ws_at<T>(i, j, d.rp, d.rp), v);
           writeback = true;
         } else {
           // fp32: add (a + B_ii) X_i here; bf16: the MFMAs already did, on
@@ -951,12 +976,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           if constexpr (!last) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = pscale * fmaf(mlt, xv[u], v[u]);
-            store8(xout + i * d.cp + j, v);
+            store8(xout + ws_at<T>(i, j, d.rp, d.cp), v);
             if constexpr (XLO) {
               float rem[8];
 #pragma unroll
               for (int u = 0; u < 8; ++u) rem[u] = v[u] - bf16_to_f32(f32_to_bf16(v[u]));
-              store8(static_cast<T*>(d.xlo) + i * d.cp + j, rem);
+              store8(static_cast<T*>(d.xlo) + ws_at<T>(i, j, d.rp, d.cp), rem);
             }
             writeback = !QT;                // fp32 also writes X^T from the stage
           } else if (!d.tall) {
@@ -1010,9 +1035,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           // the direct pass does not write its scaled values back to the stage
 #pragma unroll
           for (int u = 0; u < 8; ++u) v[u] *= gscale;
-          store8(static_cast<T*>(d.a) + j * d.rp + i, v);
+          store8(static_cast<T*>(d.a) + ws_at<T>(j, i, d.rp, d.rp), v);
         } else if constexpr (OP == kGemmPoly) {
-          store8(static_cast<T*>(d.b) + j * d.rp + i, v);
+          store8(static_cast<T*>(d.b) + ws_at<T>(j, i, d.rp, d.rp), v);
         } else if constexpr (!last) {
           store8(xtn + j * d.rp + i, v);
         }

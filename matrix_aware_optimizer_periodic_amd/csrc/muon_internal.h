@@ -74,10 +74,12 @@ struct NsDev {
   int32_t tall;      // stored block is c x r
   int64_t rows, cols, col0, ld;
   int64_t r, c, rp, cp;   // logical and padded X dims
-  // X row-major (rp x cp).  bf16: x[0], x[1] ping-pong between rounds, and
-  // the product reads its X operand from x through transposed LDS reads.
-  // fp32: x[0] only, updated in place, plus X^T (cp x rp) in xt[0], xt[1]
-  // ping-pong as the product's operand.
+  // X (rp x cp).  bf16: x[0], x[1] ping-pong between rounds, and the
+  // product reads its X operand from x through transposed LDS reads; bf16
+  // X, xlo, A and B are k-block-major (element (i, j) at
+  // ((j / 32) * rp + i) * 32 + j % 32).  fp32: row-major, x[0] only, updated
+  // in place, plus X^T (cp x rp) in xt[0], xt[1] ping-pong as the product's
+  // operand.
   void* x[2];
   void* xt[2];       // null in bf16
   void* a;           // rp x rp, X X^T
