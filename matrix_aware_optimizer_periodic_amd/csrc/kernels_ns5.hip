@@ -784,9 +784,61 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt<0>();
-  __syncthreads();
 
   // ---- epilogue -----------------------------------------------------------
+  // bf16 product of a round before the last: the next X straight from the
+  // accumulators.  In the k-block-major layout, accumulator v of a 32 x 32
+  // MFMA block holds across lanes 0-31 (and 32-63) 32 consecutive values of
+  // one row (and of the row 4 below), 64 contiguous bytes each: a 2-byte
+  // store per lane writes whole 128-byte lines, with no LDS staging and no
+  // barrier.
+  if constexpr (QT && !last) {
+    // Buffer stores: the lane's offset in a VGPR, the block's (wave-uniform)
+    // in an SGPR, the row within the block as the instruction's immediate.
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        cur ? d.x[0] : d.x[1], 0, int(d.rp * d.cp * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        d.xlo, 0, XLO ? int(d.rp * d.cp * 2) : 0, 0x00020000);
+    const float s0 = iter == 0 ? d.scale[0] : 1.0f;   // round 0 works on the unscaled M
+    const int voff = (4 * (lane >> 5) * 32 + (lane & 31)) * 2;
+    const int swm = swid / WGN, swn = swid % WGN;     // wave-uniform
+#pragma unroll
+    for (int fa = 0; fa < FM; ++fa) {
+      const int64_t ib = i0 + swm * WM + fa * 32;
+#pragma unroll
+      for (int fb = 0; fb < FN; ++fb) {
+        const int64_t jb = j0 + swn * WN + fb * 32;   // a whole 32-column block
+        const int soff = int(((jb >> 5) * d.rp + ib) * 64);
+        // Keeps this block's accumulators in AGPRs up to here: otherwise the
+        // compiler copies every accumulator to VGPRs at the loop exit, and a
+        // 128 x 256 tile no longer fits two workgroups per CU.
+        asm volatile("" : "+a"(acc[fa][fb]));
+        float lo[16];
+        if constexpr (XLO) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            lo[v] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+                rl, voff + (8 * (v >> 2) + (v & 3)) * 64, soff, 0));
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = (8 * (v >> 2) + (v & 3)) * 64;   // bytes: 4 rows apart per v & 3
+          const float x = XLO ? s0 * fmaf(ca, lo[v], acc[fa][fb][v]) : s0 * acc[fa][fb][v];
+          const uint32_t hi = f32_to_bf16(x);
+          __builtin_amdgcn_raw_buffer_store_b16(uint16_t(hi), rx, voff + row, soff, 0);
+          if constexpr (XLO)
+            __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16(x - bf16_to_f32(hi))), rl,
+                                                  voff + row, soff, 0);
+        }
+        // one block at a time: the compiler would otherwise copy every
+        // accumulator out of the AGPRs at once and run out of VGPRs
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    return;
+  }
+  __syncthreads();
+
   // Stage layout: value (r, c) of a half tile sits at r * SLD + (c ^ sw(r)),
   // sw(r) = ((r >> 4) & 7) << 2.  The transposed pass reads a column run
   // r = 8 ch + u (ch = 0..15) at fixed c; with the swizzle those 16 reads hit
