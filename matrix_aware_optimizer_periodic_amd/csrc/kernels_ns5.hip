@@ -375,11 +375,14 @@ template <> struct Raw8<float> {
 // between the two operands is valid as long as it is the same for both.
 // Accumulator element v of lane l is C[8 (v/4) + 4 (l/32) + (v%4)][l & 31].
 //
-// Epilogue, per pass over rows of the tile (as many as the workgroup's LDS
-// share holds in fp32): the waves owning them park their accumulators in
-// LDS, then all threads write the outputs in 16-byte chunks,
-// first along rows (C, or W of a wide matrix), then along columns (the
-// mirrored half of a symmetric A or B, X^T in fp32, or W of a tall matrix).
+// Epilogue.  A bf16 product before the last round stores the next X straight
+// from the accumulators (two 64-byte row runs per accumulator register in the
+// k-block-major layout).  Every other epilogue works per pass over rows of
+// the tile (as many as the workgroup's LDS share holds in fp32): the waves
+// owning them park their accumulators in LDS, then all threads write the
+// outputs in 16-byte chunks, first along rows (C, or W of a wide matrix),
+// then along columns (the mirrored half of a symmetric A or B, X^T in fp32,
+// or W of a tall matrix).
 //
 // Rounding.  The diagonal of A stays in fp32 (adiag), and the A_ii^2 term of
 // (A A)_ii and the b A_ii term use it.  B's diagonal a + B_ii (the product
@@ -440,8 +443,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // OP kGemmProductLast is the product of the last round (updates W).
   constexpr bool PROD = OP == kGemmProduct || OP == kGemmProductLast;
   constexpr bool last = OP == kGemmProductLast;
-  // bf16 product: the X operand is staged from row-major X (32 rows of k by
-  // the tile's BM columns) and read with transposed LDS loads.
+  // bf16 product: the X operand is staged as rows of X (32 rows of k by the
+  // tile's BN columns) and read with transposed LDS loads.
   constexpr bool QT = PROD && sizeof(T) == 2;
   // XLO (bf16 products with X's remainder): the a X term also takes a xlo,
   // and a round before the last stores its output's remainder back to xlo.
@@ -514,7 +517,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // wait for the prefetch in flight.  Offsets past a buffer's end read 0.
   //
   // QT: the Q part of a stage is X rows k .. k + 31, columns j0 .. j0 + BN - 1
-  // (2 BN bytes per row, CPRQ 16-byte chunks); DMA block b holds rows
+  // (2 BN bytes per row in LDS, CPRQ 16-byte chunks; in memory, BN / 32
+  // k-blocks of 32 rows x 64 bytes, 2 KB each); DMA block b holds rows
   // RPB b .. RPB b + RPB - 1 and lane l brings row RPB b + l / CPRQ, logical
   // chunk (l % CPRQ) ^ ((row & 3) << 2), which lands at physical chunk
   // l % CPRQ.  The XOR puts the four rows a transposed read touches in four
