@@ -30,6 +30,8 @@
 // checks and ragged shapes cost only the padded tiles.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "muon_internal.h"
 
 namespace muon {
@@ -455,7 +457,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // take wider tiles (more flops per staged byte).
   static_assert(BN == BM || (OP == kGemmProduct && sizeof(T) == 2), "wide tiles: bf16 product");
   constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int FM = WM / 32, FN = WN / 32;
+  // MFMA block: 16 x 16 x 32 for bf16 256-tiles, 32 x 32 x 16 (bf16) or
+  // 32 x 32 x 2 (fp32) otherwise.  At the package power limit the 16 x 16 x
+  // 32 form runs the same flops at a higher clock; the 128-tile kernels,
+  // two workgroups per CU, lack the registers for its fragment buffers.
+  constexpr int MF = sizeof(T) == 2 && BM >= 256 ? 16 : 32;
+  constexpr int FM = WM / MF, FN = WN / MF;
+  constexpr int NV = MF * MF / 64;           // accumulators per lane per block
   constexpr int ROWS = BM + BN;              // P rows then Q rows (64 bytes each)
   // Stages in the LDS ring: 4 for 256-tiles (of 160 KB), 5 for 128-tiles
   // and 3 for 128 x 256 (within 80 KB: two workgroups per CU); deeper rings
@@ -509,8 +517,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   const int nk = int(K / KT);
 
   // DMA mapping.  Instruction q of wave w fills LDS rows 16 b .. 16 b + 15 of
-  // the stage, b = w + NW q; lane l brings row 16 b + (l >> 2), logical chunk
-  // (l & 3) ^ ((l >> 4) & 3), which lands at physical chunk l & 3.
+  // the stage, b = w + NW q; lane l brings row r = 16 b + (l >> 2), logical
+  // chunk (l & 3) ^ sw(r), which lands at physical chunk l & 3.  The row
+  // swizzle sw(r) is (r >> 2) & 3 for 32 x 32 fragments (a 128-bit read then
+  // takes 32 rows at one logical chunk) and (r >> 1) & 3 for 16 x 16
+  // fragments (16 rows at each of the four chunks): measured on gfx950, each
+  // keeps its fragment reads free of bank conflicts, and the other would
+  // double their LDS cycles.
   // Blocks q < DMAP are P rows, the others Q rows.  The loads are MUBUF
   // buffer loads into LDS: unlike the FLAT form they count only against the
   // vector-memory counter, so waiting for LDS fragment reads does not also
@@ -524,12 +537,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // l % CPRQ.  The XOR puts the four rows a transposed read touches in four
   // distinct 64-byte bank groups.
   const int drow = 16 * wid + (lane >> 2);
-  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const int dchunk = (lane & 3) ^ (MF == 16 ? (lane >> 3) & 3 : (lane >> 4) & 3);
   constexpr int CPRQ = BN / 8, RPB = 64 / CPRQ;
   static_assert(!QT || (RPB * CPRQ == 64 && (RPB * NW) % 4 == 0),
                 "whole rows per DMA block; row phase of a lane fixed across its blocks");
+  // With 16 x 16 x 32 MFMAs the four lane groups of a transposed read take
+  // rows 8 apart (k 0-7, 8-15, ...) of the same columns; bit 3 of the row
+  // then also flips bit 1 of the chunk, so that two groups served together
+  // land in different banks.  A wave's blocks are 8 rows apart there, so
+  // that bit alternates with the block.
+  constexpr bool QSW8 = QT && MF == 16;
+  static_assert(!QSW8 || RPB * NW == 8, "QT swizzle: row bit 3 alternates with the DMA block");
   const int qtrow = RPB * wid + lane / CPRQ;
   const int qtchunk = (lane % CPRQ) ^ ((qtrow & 3) << 2);
+  const int qtchunk1 = qtchunk ^ (QSW8 ? 2 : 0);   // odd blocks (QSW8)
   const int64_t prow = d.rp;   // P is X, A or B: rp rows
   const int64_t qrow = QT ? d.rp : (PROD ? d.cp : d.rp);
   const u32x4_t rP = buffer_rsrc(P, prow * ld * int64_t(sizeof(T)));
@@ -545,6 +566,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
       QT ? unsigned((j0 / 32 + qtchunk / 4) * qrow * 64 + qtrow * 64 + (qtchunk % 4) * 16)
          : BLK ? unsigned((j0 + drow) * 64 + dchunk * 16)
                : unsigned((j0 + drow) * ldq * int64_t(sizeof(T))) + unsigned(dchunk * 16);
+  const unsigned offQ1 =
+      QSW8 ? unsigned((j0 / 32 + qtchunk1 / 4) * qrow * 64 + qtrow * 64 + (qtchunk1 % 4) * 16) : offQ;
   const unsigned rstrideQ = BLK ? unsigned((QT ? RPB * NW : 16 * NW) * 64)
                                 : unsigned(int64_t(16 * NW) * ldq * int64_t(sizeof(T)));
   // bytes per stage along k: P, one k-block of all prow rows (bf16) or 64;
@@ -567,7 +590,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         (LOCAL unsigned char*)(smem + (kt % NSTAGE) * STAGE + swid * 1024);
     const unsigned kb = q < DMAP ? unsigned(kc * kstepP) : unsigned(kc * kstepQ);
     const unsigned voff = q < DMAP ? offP + unsigned(q) * rstride
-                                   : offQ + unsigned(q - DMAP) * rstrideQ;
+                                   : ((q - DMAP) & 1 ? offQ1 : offQ) + unsigned(q - DMAP) * rstrideQ;
     dma16(q < DMAP ? rP : rQ, unsigned(uintptr_t(base + q * NW * 1024)), voff, unsigned(kb));
   };
   auto issue = [&](int kt) {
@@ -575,11 +598,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     for (int q = 0; q < DMA; ++q) issue_one(kt, q);
   };
 
-  f32x16_t acc[FM][FN];
+  using AccV = std::conditional_t<MF == 16, f32x4_t, f32x16_t>;
+  AccV acc[FM][FN];
 #pragma unroll
   for (int a = 0; a < FM; ++a)
 #pragma unroll
-    for (int b = 0; b < FN; ++b) acc[a][b] = (f32x16_t)(0.0f);
+    for (int b = 0; b < FN; ++b) {
+      acc[a][b] = (AccV)(0.0f);
+      // Gram and polynomial: give every accumulator its AGPRs from the start;
+      // otherwise the allocator keeps one block in VGPRs across the main loop
+      // and rotates others through a spare AGPR tuple, some 90 moves a stage.
+      if constexpr (MF == 16 && !PROD) asm volatile("" : "+a"(acc[a][b]));
+    }
+  // Row and column within an MFMA block of accumulator v of this lane.
+  auto acc_row = [&](int v) { return MF == 16 ? 4 * (lane >> 4) + v : 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); };
+  const int acc_col = lane & (MF - 1);
 
   // QT: the remainders lo_i of this wave's output rows (WM values from
   // bdiag) come by DMA too, into the ring slot of stage NSTAGE - 1, which is
@@ -597,7 +630,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   }
   for (int s0 = 0; s0 < NSTAGE - 1; ++s0) issue(s0);
 
-  const int frow = lane & 31, fsw = (lane >> 2) & 3, fhalf = lane >> 5;
+  // MFMA operand fragments: lane l holds 8 consecutive k (16 bytes) of row
+  // (or column) l % MF of the fragment, k = 8 (l / MF) .. + 7 within the
+  // k-group (16 k for 32 x 32 x 16, the stage's 32 for 16 x 16 x 32).
+  const int frow = lane & (MF - 1), fhalf = lane / MF;
+  const int fsw = MF == 16 ? (frow >> 1) & 3 : (frow >> 2) & 3;   // sw(row) of the lane's row
   // QT fragments.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of
   // a group receives element i & 3 of the 8 bytes addressed by lane
   // 4 e + (i >> 2), for e = 0..3.  Lane s of a group therefore addresses row
@@ -605,13 +642,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // c0 + i of rows k0 .. k0 + 3: four consecutive k of one column of X, as
   // the MFMA operand wants them.  Two such reads (h = 0, 1) give a lane its
   // 8 k values: k = 16 g + 8 (l >> 5) + 4 h + e, column (l & 31) of the
-  // fragment.
-  const int trow = 8 * (lane >> 5) + ((lane & 15) >> 2);          // + 16 g + 4 h
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);         // + fragment column
-  const int tsw = (trow & 3) << 2;
+  // fragment (32 x 32 x 16); k = 8 (l >> 4) + 4 h + e, column (l & 15)
+  // (16 x 16 x 32).
+  const int trow = 8 * fhalf + ((lane & 15) >> 2);                 // + 16 g + 4 h
+  const int tcol = (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);   // + fragment column
+  const int tsw = ((trow & 3) << 2) ^ (QSW8 ? ((trow >> 3) & 1) << 1 : 0);
   auto qtr = [&](const u32x4_t* sQ, int g, int f, int h, u32x4_t& out) {
     const int row = 16 * g + 4 * h + trow;
-    const int col = wn * WN + f * 32 + tcol;
+    const int col = wn * WN + f * MF + tcol;
     const int byte = row * (2 * BN) + (((col >> 3) ^ tsw) << 4) + ((col & 7) << 1);
     const LOCAL bf16x4_raw_t* p =
         (const LOCAL bf16x4_raw_t*)((const LOCAL unsigned char*)sQ + byte);
@@ -624,14 +662,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   auto frag = [&](const u32x4_t* sP, const u32x4_t* sQ, int g, u32x4_t* fa, u32x4_t* fb) {
     const int ch = (2 * g + fhalf) ^ fsw;
 #pragma unroll
-    for (int f = 0; f < FM; ++f) fa[f] = sP[(wm * WM + f * 32 + frow) * 4 + ch];
+    for (int f = 0; f < FM; ++f) fa[f] = sP[(wm * WM + f * MF + frow) * 4 + ch];
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       if constexpr (QT) {
         qtr(sQ, g, f, 0, fb[f]);
         qtr(sQ, g, f, 1, fb[f]);
       } else {
-        fb[f] = sQ[(wn * WN + f * 32 + frow) * 4 + ch];
+        fb[f] = sQ[(wn * WN + f * MF + frow) * 4 + ch];
       }
     }
   };
@@ -641,11 +679,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
                       u32x4_t* fb) {
     const int ch = (2 * g + fhalf) ^ fsw;
     if (f < FM) {
-      fa[f] = sP[(wm * WM + f * 32 + frow) * 4 + ch];
+      fa[f] = sP[(wm * WM + f * MF + frow) * 4 + ch];
     } else if constexpr (QT) {
       qtr(sQ, g, (f - FM) >> 1, (f - FM) & 1, fb[(f - FM) >> 1]);
     } else {
-      fb[f - FM] = sQ[(wn * WN + (f - FM) * 32 + frow) * 4 + ch];
+      fb[f - FM] = sQ[(wn * WN + (f - FM) * MF + frow) * 4 + ch];
     }
   };
   // MFMAs of one k-group over the flattened fragment pairs [lo, hi).
@@ -654,7 +692,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     for (int xy = 0; xy < FM * FN; ++xy) {
       if (xy < lo || xy >= hi) continue;
       const int x = xy / FN, y = xy % FN;
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (MF == 16) {
+        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, fa[x]), __builtin_bit_cast(bf16x8_t, fb[y]), acc[x][y],
+            0, 0, 0);
+      } else if constexpr (sizeof(T) == 2) {
         acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, fa[x]), __builtin_bit_cast(bf16x8_t, fb[y]), acc[x][y],
             0, 0, 0);
@@ -693,99 +735,212 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  constexpr int NXY = FM * FN;                       // fragment pairs per k-group
-  constexpr int PRE = NXY >= 16 ? 2 : 1;             // g1 pairs issued before the barrier
-  constexpr int NRD = FM + (QT ? 2 : 1) * FN;        // LDS reads per k-group
-  u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
-  // QT: remainder lo_i of the diagonal a + B_ii for row (lane & 31) of each
-  // fragment row fa, and the stage that holds those rows of X for fa = 0.
-  float dlo[FM];
-  const int kf0 = int(it.ti) * (BM / 32) + (swid / WGN) * FM;   // scalar: a uniform branch
-  {
-    wait_vmcnt<(NSTAGE - 2) * DMA>();   // stage 0 is in; stages 1 .. NSTAGE-2 may be in flight
-    bar();
-    if constexpr (QT) {
-      const float* sd = reinterpret_cast<const float*>(smem + DLO_SLOT) + wid * WM;
-#pragma unroll
-      for (int fa = 0; fa < FM; ++fa) dlo[fa] = sd[fa * 32 + (lane & 31)];
-    }
-    const u32x4_t *sP, *sQ;
-    stage_ptrs(0, sP, sQ);
-    frag(sP, sQ, 0, a0, b0);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  }
-  // Every iteration issues exactly DMA loads, so after the waits below the
-  // DMAs in flight are those of stages kt + 2 .. kt + NSTAGE - 2.  The fragment reads of stage
-  // nk (past the end) read a reloaded buffer and are never used.
-  for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MF == 16) {
+    // One k-group per stage: its 32 k feed the FM x FN 16 x 16 x 32 MFMAs,
+    // in two halves by column (y < HB, then y >= HB), each row by row.  One
+    // set of fragments, a[] and b[], is refilled with the next stage's as the
+    // current one frees up: b[y] after its last MFMA (in the last row of its
+    // half), a[x] after row x of the second half.  Each refill then has about
+    // half a stage (30-36 MFMAs) before the next stage needs it.  The reads
+    // of stage kt + 1 may start after the barrier, which comes after the
+    // first PRE MFMAs: by then every wave has issued all its reads of stage
+    // kt (during stage kt - 1), so the DMA may refill stage kt - 1's buffer.
+    constexpr int NXY = FM * FN;
+    constexpr int HB = FN / 2;                   // columns per half
+    constexpr int PRE = 2;                       // MFMAs issued before the barrier
+    constexpr int NBR = QT ? 2 : 1;              // LDS reads per B fragment
+    const int fch = fhalf ^ fsw;                 // the lane's 16-byte chunk of a P or Q row
+    u32x4_t a[FM], b[FN];
+    float dlo[FM];
+    const int kf0 = int(it.ti) * (BM / 32) + (swid / WGN) * (WM / 32);
+    auto rd_a = [&](const u32x4_t* sP, int x) { a[x] = sP[(wm * WM + x * 16 + frow) * 4 + fch]; };
+    auto rd_b = [&](const u32x4_t* sQ, int y, int h) {
+      if constexpr (QT) qtr(sQ, 0, y, h, b[y]);
+      else b[y] = sQ[(wn * WN + y * 16 + frow) * 4 + fch];
+    };
+    // MFMA i of a stage: half i / (FM HB), row, then column within the half.
+    auto ix = [&](int i) { return (i % (FM * HB)) / HB; };
+    auto iy = [&](int i) { return (i / (FM * HB)) * HB + i % HB; };
+    auto mma16 = [&](int i) {
+      const int x = ix(i), y = iy(i);
+      acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, a[x]), __builtin_bit_cast(bf16x8_t, b[y]), acc[x][y], 0, 0, 0);
+    };
     {
-      const u32x4_t *sP, *sQ;
-      stage_ptrs(kt, sP, sQ);
+      wait_vmcnt<(NSTAGE - 2) * DMA>();   // stage 0 is in; stages 1 .. NSTAGE-2 may be in flight
+      bar();
+      if constexpr (QT) {
+        const float* sd = reinterpret_cast<const float*>(smem + DLO_SLOT) + wid * WM;
 #pragma unroll
-      for (int i = 0; i < NXY; ++i) {
-        mma(a0, b0, i, i + 1);
-        if (i < NRD) frag_one(sP, sQ, 1, i, a1, b1);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int fa = 0; fa < FM; ++fa) dlo[fa] = sd[fa * 16 + (lane & 15)];
       }
+      const u32x4_t *sP, *sQ;
+      stage_ptrs(0, sP, sQ);
 #pragma unroll
-      for (int i = NXY; i < NRD; ++i) frag_one(sP, sQ, 1, i, a1, b1);
+      for (int x = 0; x < FM; ++x) rd_a(sP, x);
+#pragma unroll
+      for (int y = 0; y < FN; ++y)
+#pragma unroll
+        for (int h = 0; h < NBR; ++h) rd_b(sQ, y, h);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    // Every iteration issues exactly DMA loads, so after the wait below the
+    // DMAs in flight are those of stages kt + 2 .. kt + NSTAGE - 2.  The
+    // fragment reads of stage nk (past the end) read a reloaded buffer and
+    // are never used.
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < PRE; ++i) {
-        mma(a1, b1, i, i + 1);
+        mma16(i);
         __builtin_amdgcn_sched_barrier(0);
       }
+      wait_vmcnt<(NSTAGE - 3) * DMA>();
+      bar();
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4_t *sP, *sQ;
       if constexpr (QT) {
-        // Stage kt holds rows 32 kt .. 32 kt + 31 of X, i.e. (for one fa)
-        // X_i of this wave's output rows: add lo_i X_i with MFMAs whose P
-        // operand is diag(lo) over those 32 rows (B itself carries bf16(a +
-        // B_ii) on its diagonal).
+        // Stage kt holds rows 32 kt .. 32 kt + 31 of X: for fa = 2 m, 2 m + 1
+        // (kt = kf0 + m) the X_i of this wave's output rows.  Add lo_i X_i
+        // with MFMAs whose A operand is diag(lo) over those 16 rows (B
+        // itself carries bf16(a + B_ii) on its diagonal).
 #pragma unroll
-        for (int fa = 0; fa < FM; ++fa) {
-          if (kt == kf0 + fa) {
-            const uint32_t bits = f32_to_bf16(dlo[fa]);
+        for (int m = 0; m < FM / 2; ++m) {
+          if (kt == kf0 + m) {
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-              const int e = (lane & 31) - 16 * g - 8 * (lane >> 5);
+            for (int hh = 0; hh < 2; ++hh) {
+              const int fa = 2 * m + hh;
+              const uint32_t bits = f32_to_bf16(dlo[fa]);
+              const int e = 16 * hh + (lane & 15) - 8 * (lane >> 4);
               u32x4_t f = {0u, 0u, 0u, 0u};
 #pragma unroll
               for (int w2 = 0; w2 < 4; ++w2)
-                f[w2] = (e >= 0 && (e >> 1) == w2) ? bits << (16 * (e & 1)) : 0u;
+                f[w2] = (e >= 0 && e < 8 && (e >> 1) == w2) ? bits << (16 * (e & 1)) : 0u;
 #pragma unroll
               for (int y = 0; y < FN; ++y)
-                acc[fa][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8_t, f),
-                    __builtin_bit_cast(bf16x8_t, g ? b1[y] : b0[y]), acc[fa][y], 0, 0, 0);
+                acc[fa][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, f), __builtin_bit_cast(bf16x8_t, b[y]),
+                    acc[fa][y], 0, 0, 0);
             }
           }
         }
       }
-    }
-    wait_vmcnt<(NSTAGE - 3) * DMA>();
-    bar();
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      const u32x4_t *sP, *sQ;
       stage_ptrs(kt + 1, sP, sQ);
-      // Each slot carries up to two of the DMAs and LDS reads, alternating
-      // while both remain.
-      int nd = 0, nr = 0;
+      // After MFMA i: the DMAs of stage kt + NSTAGE - 1 in the first slots,
+      // the reads of stage kt + 1's b[y] once MFMA (FM - 1, y) is issued, and
+      // of its a[x] once row x of the second half is.
+      int nd = 0;
 #pragma unroll
       for (int i = PRE; i < NXY; ++i) {
-        mma(a1, b1, i, i + 1);
+        mma16(i);
+        const int x = ix(i), y = iy(i);
+        if (nd < DMA && i % 2 == 0) { issue_one(kt + NSTAGE - 1, nd); ++nd; }
+        if (x == FM - 1) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (nd < DMA && (nr >= NRD || nd <= nr)) { issue_one(kt + NSTAGE - 1, nd); ++nd; }
-          else if (nr < NRD) { frag_one(sP, sQ, 0, nr, a0, b0); ++nr; }
+          for (int h = 0; h < NBR; ++h) rd_b(sQ, y, h);
         }
+        if (y == FN - 1) rd_a(sP, x);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (; nd < DMA; ++nd) issue_one(kt + NSTAGE - 1, nd);
-#pragma unroll
-      for (; nr < NRD; ++nr) frag_one(sP, sQ, 0, nr, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    constexpr int NXY = FM * FN;                       // fragment pairs per k-group
+    constexpr int PRE = NXY >= 16 ? 2 : 1;             // g1 pairs issued before the barrier
+    constexpr int NRD = FM + (QT ? 2 : 1) * FN;        // LDS reads per k-group
+    u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
+    // QT: remainder lo_i of the diagonal a + B_ii for row (lane & 31) of each
+    // fragment row fa, and the stage that holds those rows of X for fa = 0.
+    float dlo[FM];
+    const int kf0 = int(it.ti) * (BM / 32) + (swid / WGN) * FM;   // scalar: a uniform branch
+    {
+      wait_vmcnt<(NSTAGE - 2) * DMA>();   // stage 0 is in; stages 1 .. NSTAGE-2 may be in flight
+      bar();
+      if constexpr (QT) {
+        const float* sd = reinterpret_cast<const float*>(smem + DLO_SLOT) + wid * WM;
+  #pragma unroll
+        for (int fa = 0; fa < FM; ++fa) dlo[fa] = sd[fa * 32 + (lane & 31)];
+      }
+      const u32x4_t *sP, *sQ;
+      stage_ptrs(0, sP, sQ);
+      frag(sP, sQ, 0, a0, b0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    // Every iteration issues exactly DMA loads, so after the waits below the
+    // DMAs in flight are those of stages kt + 2 .. kt + NSTAGE - 2.  The fragment reads of stage
+    // nk (past the end) read a reloaded buffer and are never used.
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const u32x4_t *sP, *sQ;
+        stage_ptrs(kt, sP, sQ);
+  #pragma unroll
+        for (int i = 0; i < NXY; ++i) {
+          mma(a0, b0, i, i + 1);
+          if (i < NRD) frag_one(sP, sQ, 1, i, a1, b1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  #pragma unroll
+        for (int i = NXY; i < NRD; ++i) frag_one(sP, sQ, 1, i, a1, b1);
+  #pragma unroll
+        for (int i = 0; i < PRE; ++i) {
+          mma(a1, b1, i, i + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (QT) {
+          // Stage kt holds rows 32 kt .. 32 kt + 31 of X, i.e. (for one fa)
+          // X_i of this wave's output rows: add lo_i X_i with MFMAs whose P
+          // operand is diag(lo) over those 32 rows (B itself carries bf16(a +
+          // B_ii) on its diagonal).
+  #pragma unroll
+          for (int fa = 0; fa < FM; ++fa) {
+            if (kt == kf0 + fa) {
+              const uint32_t bits = f32_to_bf16(dlo[fa]);
+  #pragma unroll
+              for (int g = 0; g < 2; ++g) {
+                const int e = (lane & 31) - 16 * g - 8 * (lane >> 5);
+                u32x4_t f = {0u, 0u, 0u, 0u};
+  #pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2)
+                  f[w2] = (e >= 0 && (e >> 1) == w2) ? bits << (16 * (e & 1)) : 0u;
+  #pragma unroll
+                for (int y = 0; y < FN; ++y)
+                  acc[fa][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                      __builtin_bit_cast(bf16x8_t, f),
+                      __builtin_bit_cast(bf16x8_t, g ? b1[y] : b0[y]), acc[fa][y], 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+      wait_vmcnt<(NSTAGE - 3) * DMA>();
+      bar();
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const u32x4_t *sP, *sQ;
+        stage_ptrs(kt + 1, sP, sQ);
+        // Each slot carries up to two of the DMAs and LDS reads, alternating
+        // while both remain.
+        int nd = 0, nr = 0;
+  #pragma unroll
+        for (int i = PRE; i < NXY; ++i) {
+          mma(a1, b1, i, i + 1);
+  #pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            if (nd < DMA && (nr >= NRD || nd <= nr)) { issue_one(kt + NSTAGE - 1, nd); ++nd; }
+            else if (nr < NRD) { frag_one(sP, sQ, 0, nr, a0, b0); ++nr; }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  #pragma unroll
+        for (; nd < DMA; ++nd) issue_one(kt + NSTAGE - 1, nd);
+  #pragma unroll
+        for (; nr < NRD; ++nr) frag_one(sP, sQ, 0, nr, a0, b0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   wait_vmcnt<0>();
 
@@ -795,7 +950,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   // MFMA block holds across lanes 0-31 (and 32-63) 32 consecutive values of
   // one row (and of the row 4 below), 64 contiguous bytes each: a 2-byte
   // store per lane writes whole 128-byte lines, with no LDS staging and no
-  // barrier.
+  // barrier.  In a 16 x 16 block each group of 16 lanes holds 16 values (32
+  // bytes) of one row, and the neighbouring block the other half of the
+  // row's 64 bytes.
   if constexpr (QT && !last) {
     // Buffer stores: the lane's offset in a VGPR, the block's (wave-uniform)
     // in an SGPR, the row within the block as the instruction's immediate.
@@ -804,29 +961,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
         d.xlo, 0, XLO ? int(d.rp * d.cp * 2) : 0, 0x00020000);
     const float s0 = iter == 0 ? d.scale[0] : 1.0f;   // round 0 works on the unscaled M
-    const int voff = (4 * (lane >> 5) * 32 + (lane & 31)) * 2;
+    const int voff = (acc_row(0) * 32 + acc_col) * 2;
     const int swm = swid / WGN, swn = swid % WGN;     // wave-uniform
 #pragma unroll
     for (int fa = 0; fa < FM; ++fa) {
-      const int64_t ib = i0 + swm * WM + fa * 32;
+      const int64_t ib = i0 + swm * WM + fa * MF;
 #pragma unroll
       for (int fb = 0; fb < FN; ++fb) {
-        const int64_t jb = j0 + swn * WN + fb * 32;   // a whole 32-column block
-        const int soff = int(((jb >> 5) * d.rp + ib) * 64);
+        const int64_t jb = j0 + swn * WN + fb * MF;   // MF columns of one 32-column block
+        const int soff = int(((jb >> 5) * d.rp + ib) * 64 + (jb & 31) * 2);
         // Keeps this block's accumulators in AGPRs up to here: otherwise the
         // compiler copies every accumulator to VGPRs at the loop exit, and a
         // 128 x 256 tile no longer fits two workgroups per CU.
         asm volatile("" : "+a"(acc[fa][fb]));
-        float lo[16];
+        float lo[NV];
+        // bytes from the lane's first row to that of accumulator v
+        auto vrow = [&](int v) { return (acc_row(v) - acc_row(0)) * 64; };
         if constexpr (XLO) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            lo[v] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-                rl, voff + (8 * (v >> 2) + (v & 3)) * 64, soff, 0));
+          for (int v = 0; v < NV; ++v)
+            lo[v] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rl, voff + vrow(v), soff, 0));
         }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = (8 * (v >> 2) + (v & 3)) * 64;   // bytes: 4 rows apart per v & 3
+        for (int v = 0; v < NV; ++v) {
+          const int row = vrow(v);
           const float x = XLO ? s0 * fmaf(ca, lo[v], acc[fa][fb][v]) : s0 * acc[fa][fb][v];
           const uint32_t hi = f32_to_bf16(x);
           __builtin_amdgcn_raw_buffer_store_b16(uint16_t(hi), rx, voff + row, soff, 0);
@@ -881,11 +1039,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
   const bool mirror_w = last && d.tall;
   // Batch sizes: as many chunks in flight as registers allow without spills
   // (the two W paths share one double buffer of 4-chunk batches).
-  constexpr int PBMAX = sizeof(T) == 4 ? (last ? 1 : 2) : (XLO && last ? 1 : 4);
+  constexpr int PBMAX = sizeof(T) == 4 ? (last ? 1 : 2) : (XLO && last ? 1 : last && MF == 16 ? 2 : 4);
   constexpr int PB = DIT < PBMAX ? DIT : PBMAX;
   constexpr int NB = DIT / PB;
   static_assert(NB * PB == DIT, "whole batches");
-  constexpr int MBMAX = sizeof(T) == 4 ? 2 : 4;
+  constexpr int MBMAX = sizeof(T) == 4 || (XLO && last && MF == 16) ? 2 : 4;
   constexpr int MB = MIT < MBMAX ? MIT : MBMAX;
   constexpr int MNB = MIT / MB;
   static_assert(MNB * MB == MIT, "whole mirror batches");
@@ -937,23 +1095,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
 #pragma unroll
           for (int fb = 0; fb < FN; ++fb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int r = rbase + fa * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3);
-              const int c = wn * WN + fb * 32 + frow;
+            for (int v = 0; v < NV; ++v) {
+              const int r = rbase + fa * MF + acc_row(v);
+              const int c = wn * WN + fb * MF + acc_col;
               stage[r * SLD + (c ^ sw(r))] = acc[fa][fb][v];
             }
       }
     } else {
 #pragma unroll
       for (int fa = 0; fa < FM; ++fa) {
-        const int rb = wm * WM + fa * 32 - half * HALF;   // block row fa, first row in this pass
+        const int rb = wm * WM + fa * MF - half * HALF;   // block row fa, first row in this pass
         if (rb >= 0 && rb < HALF) {
 #pragma unroll
           for (int fb = 0; fb < FN; ++fb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int r = rb + 8 * (v >> 2) + 4 * fhalf + (v & 3);
-              const int c = wn * WN + fb * 32 + frow;
+            for (int v = 0; v < NV; ++v) {
+              const int r = rb + acc_row(v);
+              const int c = wn * WN + fb * MF + acc_col;
               stage[r * SLD + (c ^ sw(r))] = acc[fa][fb][v];
             }
         }

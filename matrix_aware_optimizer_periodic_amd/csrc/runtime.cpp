@@ -271,6 +271,27 @@ int tile_for(int64_t r) { return r >= 1024 ? 256 : 128; }
 
 constexpr int64_t kSuperRows = 8, kSuperCols = 4;
 
+// Upper-triangle tiles (i <= j) of an nr x nr tile grid, in blocks whose
+// tiles share few operand strips (tile (i, j) reads strips i and j): bands of
+// kSuperRows tile rows; each band's own triangle (up to 36 tiles on 8
+// strips), and its rectangle with each later band in halves of kSuperRows x
+// kSuperCols tiles (32 tiles on 12 strips).  Listed column band by column
+// band, so that consecutive blocks share strips too.
+template <typename Emit> void upper_tiles_banded(int64_t nr, Emit emit) {
+  for (int64_t jb = 0; jb < nr; jb += kSuperRows)
+    for (int64_t ib = 0; ib <= jb; ib += kSuperRows) {
+      const int64_t je = std::min(nr, jb + kSuperRows);
+      if (ib == jb) {
+        for (int64_t i = ib; i < je; ++i)
+          for (int64_t j = i; j < je; ++j) emit(i, j);
+        continue;
+      }
+      for (int64_t jh = jb; jh < je; jh += kSuperCols)
+        for (int64_t i = ib; i < ib + kSuperRows; ++i)
+          for (int64_t j = jh; j < std::min(je, jh + kSuperCols); ++j) emit(i, j);
+    }
+}
+
 std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_config& cfg) {
   const size_t es = cfg.ns_precision == MUON_NS_F32 ? 4 : 2;
   const bool xlo = cfg.ns_precision == MUON_NS_BF16_COMP;
@@ -334,9 +355,12 @@ std::vector<NsChunk> plan_ns(const std::vector<Problem>& probs, const muon_confi
       const int64_t nr = d.rp / tile, nc = d.cp / tile;
       const bool tri = es == 2 && d.rp == kTriRows;
       if (tri) ch.gram_tri.items.push_back(GemmItem{k, 0, 0});
-      for (int64_t i = 0; i < nr; ++i)
-        for (int64_t j = i; j < nr; ++j)
-          ch.gemm[kGemmPoly][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+      // Polynomial: upper tiles in banded blocks.  Its tiles all cost the
+      // same when the problems do, so each XCD's contiguous share runs in
+      // step and its concurrent tiles share strips in its L2.
+      upper_tiles_banded(nr, [&](int64_t i, int64_t j) {
+        ch.gemm[kGemmPoly][t256].items.push_back(GemmItem{k, int16_t(i), int16_t(j)});
+      });
       // Gram: upper tiles in 4 x 4 super-blocks, each one XCD part below
       // (its up to 16 tiles read 8 strips of X where single rows of tiles
       // would read 17), so an XCD's concurrent tiles share strips in its L2.
