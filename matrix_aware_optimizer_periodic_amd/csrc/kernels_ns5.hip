@@ -974,6 +974,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
         // compiler copies every accumulator to VGPRs at the loop exit, and a
         // 128 x 256 tile no longer fits two workgroups per CU.
         asm volatile("" : "+a"(acc[fa][fb]));
+        if constexpr (MF == 16 && !XLO) {
+          // Lanes 2k and 2k + 1 hold columns c and c + 1 of the same four rows:
+          // a swap of two values each (DPP within groups of four lanes) gives
+          // the even lane rows 0 and 2, the odd lane rows 1 and 3, of both
+          // columns: two 4-byte stores per lane instead of four 2-byte ones.
+          const bool odd = lane & 1;
+          const float x0 = s0 * acc[fa][fb][0], x1 = s0 * acc[fa][fb][1];
+          const float x2 = s0 * acc[fa][fb][2], x3 = s0 * acc[fa][fb][3];
+          auto swap = [](float v) {
+            return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+          };
+          const float r1 = swap(odd ? x0 : x1), r2 = swap(odd ? x2 : x3);
+          const uint32_t p1 = odd ? pack_bf16x2(r1, x1) : pack_bf16x2(x0, r1);
+          const uint32_t p2 = odd ? pack_bf16x2(r2, x3) : pack_bf16x2(x2, r2);
+          const int vo = voff - (odd ? 2 : 0) + (odd ? 64 : 0);   // column c & ~1, row 0 or 1
+          __builtin_amdgcn_raw_buffer_store_b32(p1, rx, vo, soff, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(p2, rx, vo + 128, soff, 0);   // row 2 or 3
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
         float lo[NV];
         // bytes from the lane's first row to that of accumulator v
         auto vrow = [&](int v) { return (acc_row(v) - acc_row(0)) * 64; };
@@ -1118,9 +1138,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
       }
     }
     __syncthreads();
-    // rows of the tile: C[i][j .. j+7]
+    // rows of the tile: C[i][j .. j+7].  The bf16 last product of a tall
+    // matrix has nothing to do here (its W update reads the stage in the
+    // mirror pass, which applies the round's scale itself).
+    const bool skip_direct = QT && last && !XLO && d.tall;
 #pragma unroll
-    for (int bt = 0; bt < NB; ++bt) {
+    for (int bt = 0; bt < (skip_direct ? 0 : NB); ++bt) {
       if (bt + 1 < NB && need_aux) prefetch(bt + 1);
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
@@ -1235,6 +1258,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
           const int64_t j = j0 + idx / CPC, i = ib0 + (idx % CPC) * 8;
           float v[8];
           mirror_vals(idx, v);
+          if (skip_direct) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] *= pscale;
+          }
           wb[mb & 1][q].update_store(w, j * d.ld + d.col0 + i, mirror_nv(i, j), v, d.lr, wkeep);
         }
       }
