@@ -787,8 +787,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
     // Every iteration issues exactly DMA loads, so after the wait below the
     // DMAs in flight are those of stages kt + 2 .. kt + NSTAGE - 2.  The
     // fragment reads of stage nk (past the end) read a reloaded buffer and
-    // are never used.
-    for (int kt = 0; kt < nk; ++kt) {
+    // are never used.  DM >= 0: stage kf0 + DM, which also takes the
+    // diagonal remainder MFMAs of fragment rows 2 DM and 2 DM + 1.  Those four
+    // stages are peeled out of the loop (QT): conditional MFMA blocks inside
+    // it cost the product about 5% (measured).
+    auto body = [&](int kt, auto dmv) {
+      constexpr int DM = decltype(dmv)::value;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < PRE; ++i) {
@@ -800,29 +804,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
       __builtin_amdgcn_sched_barrier(0);
       const u32x4_t *sP, *sQ;
       if constexpr (QT) {
-        // Stage kt holds rows 32 kt .. 32 kt + 31 of X: for fa = 2 m, 2 m + 1
-        // (kt = kf0 + m) the X_i of this wave's output rows.  Add lo_i X_i
+        // Stage kt = kf0 + DM holds rows 32 kt .. 32 kt + 31 of X: for
+        // fa = 2 DM, 2 DM + 1 the X_i of this wave's output rows.  Add lo_i X_i
         // with MFMAs whose A operand is diag(lo) over those 16 rows (B
         // itself carries bf16(a + B_ii) on its diagonal).
+        // fragment rows 2 m and 2 m + 1 (m static after unrolling)
+        auto diag = [&](int m) {
 #pragma unroll
-        for (int m = 0; m < FM / 2; ++m) {
-          if (kt == kf0 + m) {
+          for (int hh = 0; hh < 2; ++hh) {
+            const int fa = 2 * m + hh;
+            const uint32_t bits = f32_to_bf16(dlo[fa]);
+            const int e = 16 * hh + (lane & 15) - 8 * (lane >> 4);
+            u32x4_t f = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int fa = 2 * m + hh;
-              const uint32_t bits = f32_to_bf16(dlo[fa]);
-              const int e = 16 * hh + (lane & 15) - 8 * (lane >> 4);
-              u32x4_t f = {0u, 0u, 0u, 0u};
+            for (int w2 = 0; w2 < 4; ++w2)
+              f[w2] = (e >= 0 && e < 8 && (e >> 1) == w2) ? bits << (16 * (e & 1)) : 0u;
 #pragma unroll
-              for (int w2 = 0; w2 < 4; ++w2)
-                f[w2] = (e >= 0 && e < 8 && (e >> 1) == w2) ? bits << (16 * (e & 1)) : 0u;
-#pragma unroll
-              for (int y = 0; y < FN; ++y)
-                acc[fa][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, f), __builtin_bit_cast(bf16x8_t, b[y]),
-                    acc[fa][y], 0, 0, 0);
-            }
+            for (int y = 0; y < FN; ++y)
+              acc[fa][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, f), __builtin_bit_cast(bf16x8_t, b[y]),
+                  acc[fa][y], 0, 0, 0);
           }
+        };
+        if constexpr (DM >= 0) {
+          diag(DM);
+        } else if constexpr (DM == -2) {   // the stage decides at run time
+#pragma unroll
+          for (int m = 0; m < FM / 2; ++m)
+            if (kt == kf0 + m) diag(m);
         }
       }
       stage_ptrs(kt + 1, sP, sQ);
@@ -845,6 +854,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void ns_gemm_kernel(
 #pragma unroll
       for (; nd < DMA; ++nd) issue_one(kt + NSTAGE - 1, nd);
       __builtin_amdgcn_sched_barrier(0);
+    };
+    using NoDiag = std::integral_constant<int, -1>;
+    if constexpr (QT && !last) {
+      static_assert(FM == 8, "four diagonal stages of two fragment rows each");
+      // the wave's output rows are rows of X inside K, so kf0 + 3 < nk
+      int kt = 0;
+      for (; kt < kf0; ++kt) body(kt, NoDiag{});
+      body(kt, std::integral_constant<int, 0>{});
+      body(kt + 1, std::integral_constant<int, 1>{});
+      body(kt + 2, std::integral_constant<int, 2>{});
+      body(kt + 3, std::integral_constant<int, 3>{});
+      for (kt += 4; kt < nk; ++kt) body(kt, NoDiag{});
+    } else if constexpr (QT) {
+      // The last product keeps the test inside its loop: peeled, the
+      // diagonal stages cost its weight-update epilogue registers (a spill).
+      for (int kt = 0; kt < nk; ++kt) body(kt, std::integral_constant<int, -2>{});
+    } else {
+      for (int kt = 0; kt < nk; ++kt) body(kt, NoDiag{});
     }
   } else {
     constexpr int NXY = FM * FN;                       // fragment pairs per k-group
