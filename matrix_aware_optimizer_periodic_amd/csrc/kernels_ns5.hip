@@ -353,9 +353,9 @@ template <> struct Raw8<float> {
 
 // GEMM tile C[i0.., j0..] = sum_k P[i][k] Q[j][k] on MFMA, BM x BN per
 // workgroup of 2 x 2 waves (one per SIMD), each wave (BM/2) x (BN/2) built
-// from 32 x 32 MFMA blocks; a 256-tile wave holds its 128 x 128 fp32
-// accumulators in the 256 AGPRs.  BN = BM except for the 128 x 256 bf16
-// product tiles of short-K problems.
+// from MFMA blocks (16 x 16 x 32 for bf16 256-tiles, 32 x 32 otherwise); a
+// 256-tile wave holds its 128 x 128 fp32 accumulators in the 256 AGPRs.
+// BN = BM except for the 128 x 256 bf16 product tiles of short-K problems.
 //
 // Operand staging.  The k loop runs over stages of 64 bytes of k (32 bf16 or
 // 16 fp32; in bf16 one k-block of the operand's layout) for all BM + BN rows
@@ -363,14 +363,14 @@ template <> struct Raw8<float> {
 // 256-tiles, 5 for 128-tiles, 3 for 128 x 256).  Global data goes straight to LDS (MUBUF
 // buffer_load ... lds: each lane's 16 bytes land at the wave's LDS base +
 // 16 * lane), issued NSTAGE - 1 stages ahead of its use, so no registers
-// hold operands in flight.  A 64-byte LDS row holds four 16-byte chunks;
-// chunk c of row r sits at position c ^ ((r >> 2) & 3).  gfx950 serves a
-// 128-bit LDS read in groups of 16 lanes over 64 banks, and with this
-// placement the 16 consecutive rows such a group reads at one logical chunk
-// fall on 16 distinct bank groups.  The bf16 product stages its X operand
-// as rows of X instead (see QT below) and reads it transposed.
+// hold operands in flight.  A 64-byte LDS row holds four 16-byte chunks,
+// placed by a row swizzle (the DMA mapping below) so that the rows a 128-bit
+// fragment read takes at once fall on distinct bank groups.  The bf16
+// product stages its X operand as rows of X instead (see QT below) and
+// reads it transposed.
 //
-// MFMA operand layout used (both 32 x 32 variants): lane l supplies row
+// MFMA operand layout of the 32 x 32 variants (the 16 x 16 x 32 one is given
+// with the fragment reads below): lane l supplies row
 // (l & 31) of P and of Q; its k values are the 16-byte chunk 2g + (l >> 5) of
 // k-group g.  bf16 32x32x16 consumes the chunk's 8 values at once; fp32
 // 32x32x2 consumes its 4 values over 4 instructions.  Any pairing of k
